@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Chunked KDA prefill benchmark on one MI355X.
+
+One step is one whole prefill (intra-chunk kernel, then the recurrent inter-chunk
+kernel) of the H=64, T=8192, K=V=128 bf16 workload with every input already in
+device memory. Prints one JSON line with tokens/s, the dominant kernel's roofline
+and the fp64 CPU oracle timed on the host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "fixed_h64_t8192"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Algorithmic bytes per (token, head) of each kernel at K = V = 128 (bf16 io):
+#  intra: reads q, k (bf16) + g (fp32) + beta = 2*128 + 2*128 + 4*128 + 4 = 1028,
+#         writes its per-chunk record 14848 B / 16 tokens = 928;
+#  inter: reads the record (928) and v (256), writes out (256), plus the fp32
+#         final state (and initial state, if any) per (sequence, head).
+INTRA_BYTES_PER_TH = 1028 + 928
+INTER_BYTES_PER_TH = 928 + 256 + 256
+STATE_BYTES = 128 * 128 * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    return ap.parse_args()
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_04_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, digest: str, launches_units: float):
+    """HBM bytes per launch from a committed counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{WORKLOAD}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("source_digest") != digest:
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w):
+    """The fp64 oracle as it stands, on the host cores, over the whole workload (it
+    finishes in seconds on a many-core host; the sample is every head)."""
+    import oracle
+
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], want_out=True, want_state=True)
+    dt = time.perf_counter() - t0
+    return {
+        "value": w.total_tokens / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"whole workload ({w.heads} heads x {w.total_tokens} tokens), one run, {dt:.2f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and sequences would shard without communication; see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from linear_attention_04_amd import inputs, kda
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    kda.load_library()
+    w = inputs.WORKLOADS[WORKLOAD]
+    x = inputs.generate(w)
+    dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
+                         if bf else torch.from_numpy(a).to("cuda"))
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    g, beta = dev(x["g"], False), dev(x["beta"], False)
+    T, H = w.total_tokens, w.heads
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((1, H, 128, 128), dtype=torch.float32, device="cuda")
+    dims = kda.make_dims(q, v)
+    ws = kda.workspace_for(dims, "cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(e0=None, e1=None, e2=None):
+        if e0 is not None:
+            e0.record(stream)
+        st = kda.kda_intra_chunk(q.data_ptr(), k.data_ptr(), g.data_ptr(), beta.data_ptr(), None, dims,
+                                 ws.data_ptr(), ws.numel(), sp)
+        if e1 is not None:
+            e1.record(stream)
+        st2 = kda.kda_inter_chunk(v.data_ptr(), None, None, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
+                                  ws.numel(), sp)
+        if e2 is not None:
+            e2.record(stream)
+        if st or st2:
+            raise kda.KdaError(st or st2, "prefill")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(out.float()).all()):
+        print("non-finite output", file=sys.stderr)
+        return 1
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(*e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    intra_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    inter_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = wall * 1e3 / args.steps
+
+    counts = inputs.algorithmic_counts(w)
+    th = T * H
+    tokens_s = T / (ms_step * 1e-3)
+    tflops = counts["flops"] / (ms_step * 1e-3) / 1e12
+    path_gbs = counts["bytes"] / (ms_step * 1e-3) / 1e9
+
+    kernels = {
+        "intra": (intra_ms, INTRA_BYTES_PER_TH * th, ["kda_intra_bf16.hip", "kda_device.h", "kda_chunks.h"]),
+        "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * H,
+                  ["kda_inter_bf16.hip", "kda_device.h", "kda_chunks.h"]),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_bytes, dom_src = kernels[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    digest = source_digest(dom_src)
+    traffic = traffic_for(dom, digest, 1)
+
+    rec = {
+        "metric": "KDA prefill tokens/s + TFLOP/s (% roofline), H=64 T=8192 K=V=128 bf16",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "heads": H, "tokens": T, "head_k": 128, "head_v": 128,
+                   "num_seqs": 1, "initial_state": False, "chunk": 16},
+        "tflops": tflops,
+        "tflops_frac": tflops / BF16_PEAK_TFLOPS,
+        "path_hbm": {"algorithmic_bytes": counts["bytes"], "achieved": path_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": path_gbs / HBM_PEAK_GBS},
+        "kernels_ms": {"intra": intra_ms, "inter": inter_ms},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": dom_bytes, "source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

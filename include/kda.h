@@ -1,0 +1,116 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked KDA prefill library (libkda.so).
+ *
+ * Kimi Delta Attention (KDA) keeps one fixed-size K x V recurrent state per head;
+ * every token updates it instead of appending to a key/value cache
+ * (akiraxclaw.com "Kimi K3 開源基礎設施：三個專案怎麼分工？", section
+ * "FlashKDA：先把 KDA kernel 跑快"; augursoft.site "Kimi K3 的三個系統設計",
+ * section "第一個設計"). For token t of a sequence, with alpha_t = exp(g_t):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t.
+ *
+ * Prefill evaluates this over whole sequences in 16-token chunks with two kernels,
+ * one token-parallel over (chunk, head) and one that carries the state from chunk
+ * to chunk (augursoft.site "Kimi K3 的三個系統設計", section
+ * "為什麼 FlashKDA 選擇 16-token chunks": 16-token chunks, a 16 x 16 matrix
+ * inversion, and work split into two kernels by parallelism). The fast path is
+ * head dimension K = V = 128 (tech-noisy.com, section
+ * "MoE通信とアテンション:MoonEPとFlashKDA", which states that restriction).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller. The library
+ *    allocates and frees nothing, keeps no global state and is reentrant.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream) and the call returns without waiting. Buffers must stay
+ *    alive until the stream has passed the call.
+ *  - Argument checks happen on the host before anything is enqueued; a negative
+ *    status means nothing was launched. No C++ exception crosses the ABI.
+ *  - Contents of cu_seqlens are not read on the host (they live on the device);
+ *    they must satisfy cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T.
+ *
+ * Layouts (row-major, contiguous, T = total_tokens over all packed sequences):
+ *    q, k     [T, H, K]      io dtype     (q already scaled; the library applies none)
+ *    v        [T, H, V]      io dtype
+ *    out      [T, H, V]      io dtype     (bf16 results are rounded to nearest even)
+ *    g        [T, H, K]      fp32         natural-log per-channel decay, alpha = exp(g)
+ *    beta     [T, H]         fp32
+ *    states   [N, H, K, V]   fp32         initial_state (read), final_state (written)
+ *    cu_seqlens [N + 1]      int32        sequence boundaries; NULL means one sequence
+ * Every data pointer must be 16-byte aligned.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* io dtype of q, k, v and out */
+#define KDA_IO_BF16 0
+#define KDA_IO_F32 1
+
+/* status codes */
+#define KDA_OK 0
+#define KDA_ERR_ARG (-1)         /* NULL required pointer, bad sizes, or num_seqs != 1 with NULL cu_seqlens */
+#define KDA_ERR_UNSUPPORTED (-2) /* (K, V, io dtype) combination without a kernel */
+#define KDA_ERR_ALIGN (-3)       /* a data pointer is not 16-byte aligned */
+#define KDA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than kda_workspace_bytes() */
+#define KDA_ERR_LAUNCH (-5)      /* the HIP runtime reported an error at launch */
+
+/* Problem sizes. Supported: io bf16 with K = V = 128; io fp32 with K = V in {16, 32, 64, 128}. */
+typedef struct kda_dims {
+    int64_t total_tokens; /* T >= 0, summed over the packed sequences */
+    int32_t num_heads;    /* H >= 1 */
+    int32_t head_k;       /* K */
+    int32_t head_v;       /* V */
+    int32_t num_seqs;     /* N >= 1 */
+    int32_t io_dtype;     /* KDA_IO_BF16 or KDA_IO_F32 */
+    int32_t reserved;     /* must be 0 */
+} kda_dims_t;
+
+/* Bytes of device workspace kda_chunk_prefill / kda_intra_chunk / kda_inter_chunk need
+ * for these sizes, or 0 if the sizes are invalid or unsupported. Host-only. */
+size_t kda_workspace_bytes(const kda_dims_t *dims);
+
+/* Whole prefill: chunk table (packed input only), intra-chunk kernel, then the
+ * recurrent inter-chunk kernel, all on `stream`.
+ *  initial_state NULL: every sequence starts from S = 0.
+ *  final_state NULL: final states are not written.
+ * Returns KDA_OK or a negative status. */
+int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const int32_t *cu_seqlens,
+                      const float *initial_state, void *out, float *final_state,
+                      const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* First half of kda_chunk_prefill: builds the chunk table (if cu_seqlens is not NULL)
+ * and, for every 16-token chunk of every head, the in-chunk gate prefix sums, the
+ * 16 x 16 unit lower triangular inverse and the chunk factors, written to
+ * `workspace` in the library's own layout (not part of the ABI; read it only
+ * through kda_inter_chunk with the same dims and cu_seqlens). */
+int kda_intra_chunk(const void *q, const void *k, const float *g, const float *beta,
+                    const int32_t *cu_seqlens, const kda_dims_t *dims, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Second half: consumes the workspace written by kda_intra_chunk (same dims, same
+ * cu_seqlens, enqueued after it), carries each (sequence, head) state across its
+ * chunks, writes out and, if not NULL, final_state. */
+int kda_inter_chunk(const void *v, const int32_t *cu_seqlens, const float *initial_state,
+                    void *out, float *final_state, const kda_dims_t *dims,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

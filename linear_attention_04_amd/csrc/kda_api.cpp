@@ -1,0 +1,164 @@
+// kda_api.cpp -- C ABI entry points of libkda: argument checks, workspace layout and
+// kernel launches. Nothing here touches the device before every check has passed.
+#include <hip/hip_runtime.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported(const kda_dims_t *d) {
+    if (d->io_dtype == KDA_IO_BF16) return d->head_k == 128 && d->head_v == 128;
+    if (d->io_dtype == KDA_IO_F32)
+        return d->head_k == d->head_v &&
+               (d->head_k == 16 || d->head_k == 32 || d->head_k == 64 || d->head_k == 128);
+    return false;
+}
+
+int check_pointers(std::initializer_list<const void *> required, std::initializer_list<const void *> optional) {
+    for (const void *p : required) {
+        if (p == nullptr) return KDA_ERR_ARG;
+    }
+    for (const void *p : required) {
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    for (const void *p : optional) {
+        if (p != nullptr && !aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    return KDA_OK;
+}
+
+int check_common(const kda_dims_t *dims, const int32_t *cu_seqlens, void *ws, size_t ws_bytes, Geometry *geo) {
+    const int st = make_geometry(dims, geo);
+    if (st != KDA_OK) return st;
+    if (cu_seqlens == nullptr && dims->num_seqs != 1) return KDA_ERR_ARG;
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_ALIGN;
+    if (ws == nullptr || ws_bytes < geo->total_bytes) return KDA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
+
+}  // namespace
+
+int make_geometry(const kda_dims_t *d, Geometry *g) {
+    if (d == nullptr || g == nullptr) return KDA_ERR_ARG;
+    if (d->total_tokens < 0 || d->num_heads < 1 || d->head_k < 1 || d->head_v < 1 || d->num_seqs < 1 ||
+        d->reserved != 0)
+        return KDA_ERR_ARG;
+    if (d->total_tokens > (int64_t)INT32_MAX || d->num_seqs > (1 << 24) || d->num_heads > (1 << 16))
+        return KDA_ERR_ARG;
+    if (!supported(d)) return KDA_ERR_UNSUPPORTED;
+    g->T = d->total_tokens;
+    g->H = d->num_heads;
+    g->K = d->head_k;
+    g->V = d->head_v;
+    g->N = d->num_seqs;
+    g->io = d->io_dtype;
+    // sum_n ceil(len_n / 16) <= (T + 15 N) / 16
+    g->max_chunks = (g->T + 15 * (int64_t)g->N) / kChunk;
+    if (g->max_chunks > (int64_t)INT32_MAX / 2) return KDA_ERR_ARG;
+    if ((int64_t)g->N * g->H > (int64_t)INT32_MAX / 64) return KDA_ERR_ARG;
+    g->record_bytes = d->io_dtype == KDA_IO_BF16 ? (size_t)kRecBytesBf16 : rec_bytes_f32(g->K);
+    g->off_chunk_off = 0;
+    g->off_chunk_seq = align_up(sizeof(int32_t) * ((size_t)g->N + 1));
+    g->off_records = g->off_chunk_seq + align_up(sizeof(int32_t) * (size_t)g->max_chunks);
+    g->total_bytes = g->off_records + (size_t)g->max_chunks * (size_t)g->H * g->record_bytes;
+    return KDA_OK;
+}
+
+}  // namespace kda
+
+using kda::Geometry;
+
+extern "C" {
+
+size_t kda_workspace_bytes(const kda_dims_t *dims) {
+    Geometry geo;
+    if (kda::make_geometry(dims, &geo) != KDA_OK) return 0;
+    return geo.total_bytes;
+}
+
+int kda_intra_chunk(const void *q, const void *k, const float *g, const float *beta,
+                    const int32_t *cu_seqlens, const kda_dims_t *dims, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = kda::check_common(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st != KDA_OK) return st;
+    if (geo.T > 0) {
+        st = kda::check_pointers({q, k, g, beta}, {});
+        if (st != KDA_OK) return st;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cu_seqlens != nullptr) {
+        st = kda::launch_status(kda::launch_chunk_table(cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    if (geo.T == 0) return KDA_OK;
+    if (geo.io == KDA_IO_BF16)
+        return kda::launch_status(kda::launch_intra_bf16(q, k, g, beta, cu_seqlens, geo, workspace, s));
+    return kda::launch_status(kda::launch_intra_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                                    g, beta, cu_seqlens, geo, workspace, s));
+}
+
+int kda_inter_chunk(const void *v, const int32_t *cu_seqlens, const float *initial_state, void *out,
+                    float *final_state, const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    Geometry geo;
+    int st = kda::check_common(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st != KDA_OK) return st;
+    if (geo.T > 0) {
+        st = kda::check_pointers({v, out}, {initial_state, final_state});
+    } else {
+        st = kda::check_pointers({}, {v, out, initial_state, final_state});
+    }
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (geo.io == KDA_IO_BF16)
+        return kda::launch_status(
+            kda::launch_inter_bf16(v, cu_seqlens, initial_state, out, final_state, geo, workspace, s));
+    return kda::launch_status(kda::launch_inter_f32(static_cast<const float *>(v), cu_seqlens, initial_state,
+                                                    static_cast<float *>(out), final_state, geo, workspace, s));
+}
+
+int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const int32_t *cu_seqlens, const float *initial_state, void *out, float *final_state,
+                      const kda_dims_t *dims, void *workspace, size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = kda::check_common(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st != KDA_OK) return st;
+    if (geo.T > 0) {
+        st = kda::check_pointers({q, k, v, g, beta, out}, {initial_state, final_state});
+    } else {
+        st = kda::check_pointers({}, {q, k, v, g, beta, out, initial_state, final_state});
+    }
+    if (st != KDA_OK) return st;
+    st = kda_intra_chunk(q, k, g, beta, cu_seqlens, dims, workspace, workspace_bytes, stream);
+    if (st != KDA_OK) return st;
+    return kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state, dims, workspace, workspace_bytes,
+                           stream);
+}
+
+const char *kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_ARG: return "invalid argument (NULL pointer, bad sizes, or num_seqs != 1 without cu_seqlens)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head size / io dtype combination";
+    case KDA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_workspace_bytes()";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// kda_device.h -- device helpers shared by the gfx950 KDA kernels.
+//
+// Lane layouts used throughout (one 64-lane wave, lane l, c = l & 15, grp = l >> 4):
+//  * accumulator ("D") layout of a 16x16 MFMA tile: lane l holds rows 4*grp + i
+//    (i = 0..3) of column c;
+//  * A operand of v_mfma_f32_16x16x16_bf16: lane l holds row c, reduction indices
+//    4*grp + i; B operand: column c, reduction indices 4*grp + i. A D-layout tile
+//    converted to bf16 is therefore directly a B operand;
+//  * A / B operands of v_mfma_f32_16x16x32_bf16: row (A) or column (B) c, eight
+//    reduction indices per lane. Which eight the hardware pairs is irrelevant as
+//    long as A and B use the same (lane group, element) -> index assignment, which
+//    the kernels guarantee by building both operands from the same channel set.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 as_s16x4(bf16x4 x) { return __builtin_bit_cast(s16x4, x); }
+
+// Round-to-nearest-even fp32 -> bf16 (hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+__device__ __forceinline__ float from_bf16(__bf16 x) { return static_cast<float>(x); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    bf16x4 r;
+    r[0] = to_bf16(x[0]); r[1] = to_bf16(x[1]); r[2] = to_bf16(x[2]); r[3] = to_bf16(x[3]);
+    return r;
+}
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): ~16 significant bits in two bf16 parts.
+__device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = to_bf16(x[i]);
+        lo[i] = to_bf16(x[i] - from_bf16(hi[i]));
+    }
+}
+
+// DPP: value of lane (l - N) within the same 16-lane row, or 0 where that lane is
+// outside the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
+}
+
+// DPP: value of lane N of this lane's 16-lane row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Inclusive prefix sum over the 16 lanes of each row (lane c gets x_0 + ... + x_c).
+__device__ __forceinline__ float row_inclusive_sum(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+// Map a linear workgroup id so that consecutive ids land on the same XCD group:
+// the dispatcher deals workgroups to the 8 XCDs round robin (id % 8), so the
+// `per_unit` workgroups that share one unit of data (e.g. the V tiles of one
+// head) are placed at ids unit_slot + 8 * k and all run behind one L2.
+__device__ __forceinline__ void xcd_unit_split(int id, int per_unit, int &unit, int &member) {
+    const int xcd = id & 7;
+    const int rest = id >> 3;
+    member = rest % per_unit;
+    unit = (rest / per_unit) * 8 + xcd;
+}
+
+}  // namespace kda

@@ -51,6 +51,7 @@ class Workload:
     gate_scale: float
     has_initial_state: bool
     num_seqs: int = 1
+    lengths: tuple | None = None  # explicit sequence lengths (else drawn, see seq_lengths)
 
     @property
     def bf16(self) -> bool:
@@ -69,12 +70,17 @@ WORKLOADS = {
 }
 
 
-def custom_workload(name: str, seed: int, heads: int, total_tokens: int, head_k: int = 128,
-                    head_v: int = 128, io_dtype: str = "bf16", gate_scale: float = 0.1,
-                    has_initial_state: bool = False, num_seqs: int = 1) -> Workload:
-    """A workload with the standard value recipe at other sizes (parity tests)."""
+def custom_workload(name: str, seed: int, heads: int, total_tokens: int | None = None,
+                    head_k: int = 128, head_v: int = 128, io_dtype: str = "bf16",
+                    gate_scale: float = 0.1, has_initial_state: bool = False, num_seqs: int = 1,
+                    lengths=None) -> Workload:
+    """A workload with the standard value recipe at other sizes (parity tests).
+    ``lengths`` fixes the packed sequence lengths (total_tokens and num_seqs follow)."""
+    if lengths is not None:
+        lengths = tuple(int(n) for n in lengths)
+        total_tokens, num_seqs = sum(lengths), len(lengths)
     return Workload(name, seed, heads, total_tokens, head_k, head_v, io_dtype, gate_scale,
-                    has_initial_state, num_seqs)
+                    has_initial_state, num_seqs, lengths)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -133,6 +139,8 @@ def num_blocks(w: Workload) -> int:
 def seq_lengths(w: Workload) -> np.ndarray:
     """Per-sequence lengths. Several sequences: cut points drawn uniformly without
     replacement, redrawn until every length is >= 64 and none is a multiple of 16."""
+    if w.lengths is not None:
+        return np.array(w.lengths, dtype=np.int64)
     if w.num_seqs == 1:
         return np.array([w.total_tokens], dtype=np.int64)
     rng = np.random.default_rng([w.seed, _LENGTH_STREAM])

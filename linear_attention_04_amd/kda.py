@@ -1,0 +1,189 @@
+"""Python binding of libkda.so (include/kda.h).
+
+The functions named like the C entry points take raw device pointers (ints) and a
+``KdaDims``; :func:`chunk_prefill` is the torch-facing convenience wrapper that
+allocates outputs and workspace with torch and passes torch's current stream.
+Both only marshal arguments: every step of the computation runs in the HIP
+kernels of libkda.so, and there is no fallback when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_IO_BF16 = 0
+KDA_IO_F32 = 1
+KDA_OK = 0
+KDA_ERR_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_ALIGN = -3
+KDA_ERR_WORKSPACE = -4
+KDA_ERR_LAUNCH = -5
+
+EXPORTS = (
+    "kda_workspace_bytes",
+    "kda_chunk_prefill",
+    "kda_intra_chunk",
+    "kda_inter_chunk",
+    "kda_status_string",
+    "kda_version",
+)
+
+
+class KdaDims(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64),
+        ("num_heads", ctypes.c_int32),
+        ("head_k", ctypes.c_int32),
+        ("head_v", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kda_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m linear_attention_04_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dims_p = ctypes.POINTER(KdaDims)
+    lib.kda_workspace_bytes.argtypes = [dims_p]
+    lib.kda_workspace_bytes.restype = sz
+    lib.kda_chunk_prefill.argtypes = [p, p, p, p, p, p, p, p, p, dims_p, p, sz, p]
+    lib.kda_chunk_prefill.restype = i32
+    lib.kda_intra_chunk.argtypes = [p, p, p, p, p, dims_p, p, sz, p]
+    lib.kda_intra_chunk.restype = i32
+    lib.kda_inter_chunk.argtypes = [p, p, p, p, p, dims_p, p, sz, p]
+    lib.kda_inter_chunk.restype = i32
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def kda_workspace_bytes(dims: KdaDims) -> int:
+    return int(load_library().kda_workspace_bytes(ctypes.byref(dims)))
+
+
+def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, dims: KdaDims,
+                      workspace, workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                                final_state, ctypes.byref(dims), workspace,
+                                                workspace_bytes, stream))
+
+
+def kda_intra_chunk(q, k, g, beta, cu_seqlens, dims: KdaDims, workspace, workspace_bytes: int,
+                    stream) -> int:
+    return int(load_library().kda_intra_chunk(q, k, g, beta, cu_seqlens, ctypes.byref(dims),
+                                              workspace, workspace_bytes, stream))
+
+
+def kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state, dims: KdaDims, workspace,
+                    workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state,
+                                              ctypes.byref(dims), workspace, workspace_bytes, stream))
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_version() -> int:
+    return int(load_library().kda_version())
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrapper
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_dims(q, v, cu_seqlens=None) -> KdaDims:
+    import torch
+
+    T, H, K = q.shape
+    V = v.shape[2]
+    io = KDA_IO_BF16 if q.dtype == torch.bfloat16 else KDA_IO_F32
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    return KdaDims(T, H, K, V, N, io, 0)
+
+
+def workspace_for(dims: KdaDims, device):
+    import torch
+
+    nbytes = kda_workspace_bytes(dims)
+    if nbytes == 0:
+        raise KdaError(KDA_ERR_UNSUPPORTED, "kda_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state):
+    import torch
+
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t, dt in (("k", k, io), ("v", v, io), ("g", g, torch.float32), ("beta", beta, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("initial_state must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens),
+                    ("initial_state", initial_state)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    T, H, K = q.shape
+    if k.shape != (T, H, K) or g.shape != (T, H, K) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("shape mismatch: q, k, g [T,H,K], v [T,H,V], beta [T,H]")
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None,
+                  final_state=True, workspace=None, stream=None):
+    """Chunked KDA prefill on the current device.
+
+    q, k: [T, H, K]; v: [T, H, V] (bf16 or fp32); g: [T, H, K] fp32; beta: [T, H] fp32;
+    cu_seqlens: int32 [N+1] or None; initial_state: [N, H, K, V] fp32 or None.
+    final_state: True to allocate and return it, a tensor to write into, or None.
+    Returns (out, final_state).
+    """
+    import torch
+
+    _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
+    dims = make_dims(q, v, cu_seqlens)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if final_state is True:
+        final_state = torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
+                                  dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(dims, q.device)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    st = kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                           _ptr(initial_state), _ptr(out), _ptr(final_state), dims, _ptr(workspace),
+                           workspace.numel(), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_prefill")
+    return out, final_state

@@ -1,0 +1,46 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times (one kda_chunk_prefill call over the whole batch). The 8192-token workloads
+are compared element by element over every head; the 131072-token workload on a
+sample of heads, which the oracle evaluates one by one."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_04_amd import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_04_amd import kda
+
+    kda.load_library()
+
+
+def _run(name, keep):
+    w = inputs.WORKLOADS[name]
+    print(f"workload {name}: heads kept for the oracle {keep}", flush=True)
+    dev, host = gu.generate_on_device(w, keep)
+    out, fs = gu.run_gpu(dev)
+    packed = w.num_seqs > 1
+    ro, rs = oracle.prefill(host["q"], host["k"], host["v"], host["g"], host["beta"],
+                            cu_seqlens=host["cu_seqlens"] if packed else None,
+                            initial_state=host["initial_state"])
+    got_o = gu.to_host(out[:, keep])
+    got_s = gu.to_host(fs[:, keep])
+    gu.assert_close("out", got_o, ro, True)
+    gu.assert_close("final_state", got_s, rs, True)
+
+
+@pytest.mark.parametrize("name", ["fixed_h64_t8192", "fixed_h96_t8192_s0", "varlen_h96_t8192_n8"])
+def test_fullsize_all_heads(name):
+    _run(name, list(range(inputs.WORKLOADS[name].heads)))
+
+
+def test_fullsize_long_context_sampled_heads():
+    _run("long_h64_t131072_s0", [0, 21, 42, 63])

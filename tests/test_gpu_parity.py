@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes here finish in seconds on the oracle and span several chunks, several heads
+and ragged tails; the full-size workloads are in test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+
+from linear_attention_04_amd import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_04_amd import kda
+
+    kda.load_library()  # fails loudly when the HIP library is missing
+
+
+def _case(name, seed, H, T=None, K=128, io="bf16", state=False, gate=0.1, lengths=None):
+    w = inputs.custom_workload(name, seed, heads=H, total_tokens=T, head_k=K, head_v=K, io_dtype=io,
+                               gate_scale=gate, has_initial_state=state, lengths=lengths)
+    return w, inputs.generate(w)
+
+
+def _check(w, x, packed):
+    print(f"case {w.name}: H={w.heads} T={w.total_tokens} K={w.head_k} io={w.io_dtype} N={w.num_seqs}",
+          flush=True)
+    d = gu.upload(x, w.bf16, packed)
+    out, fs = gu.run_gpu(d)
+    ro, rs = gu.run_oracle(x, packed)
+    gu.assert_close("out", gu.to_host(out), ro, w.bf16)
+    gu.assert_close("final_state", gu.to_host(fs), rs, w.bf16)
+    return d, out, fs
+
+
+def test_tiny_f32_workload():
+    w = inputs.WORKLOADS["tiny_f32_h2_t64_d16"]
+    _check(w, inputs.generate(w), False)
+
+
+@pytest.mark.parametrize("K", [16, 32, 64, 128])
+def test_f32_ragged(K):
+    w, x = _case(f"f32_k{K}", 30 + K, H=3, T=53, K=K, io="f32", state=True)
+    _check(w, x, False)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100, 333])
+def test_bf16_lengths(T):
+    w, x = _case(f"bf16_t{T}", 40 + T, H=5, T=T, state=True)
+    _check(w, x, False)
+
+
+def test_bf16_zero_state_many_heads():
+    w, x = _case("bf16_h9", 7, H=9, T=520)
+    _check(w, x, False)
+
+
+def test_bf16_packed_ragged():
+    w, x = _case("bf16_packed", 8, H=4, state=True, lengths=[1, 15, 16, 17, 47, 0, 64, 100, 3])
+    _check(w, x, True)
+
+
+def test_f32_packed():
+    w, x = _case("f32_packed", 9, H=2, K=32, io="f32", state=True, lengths=[20, 5, 0, 33])
+    _check(w, x, True)
+
+
+def test_long_gate_workload_shape_small():
+    w, x = _case("bf16_long_gate", 11, H=2, T=2000, state=True, gate=0.02)
+    _check(w, x, False)
+
+
+def test_null_initial_state_equals_zeros_bitwise():
+    torch = gu.torch_mod()
+    w, x = _case("bf16_zero", 12, H=3, T=77)
+    d = gu.upload(x, True, False)
+    out_a, fs_a = gu.run_gpu(d)
+    d["initial_state"] = torch.zeros((1, 3, 128, 128), dtype=torch.float32, device="cuda")
+    out_b, fs_b = gu.run_gpu(d)
+    assert torch.equal(out_a, out_b) and torch.equal(fs_a, fs_b)
+
+
+def test_null_final_state_accepted():
+    torch = gu.torch_mod()
+    w, x = _case("bf16_nofinal", 13, H=2, T=50, state=True)
+    d = gu.upload(x, True, False)
+    out_a, _ = gu.run_gpu(d)
+    out_b, fs_b = gu.run_gpu(d, final_state=None)
+    assert fs_b is None and torch.equal(out_a, out_b)
+
+
+def test_deterministic_bitwise():
+    torch = gu.torch_mod()
+    w, x = _case("bf16_det", 14, H=6, T=300, state=True)
+    d = gu.upload(x, True, False)
+    runs = [gu.run_gpu(d) for _ in range(3)]
+    for out, fs in runs[1:]:
+        assert torch.equal(out, runs[0][0]) and torch.equal(fs, runs[0][1])
+
+
+def test_packed_equals_separate_calls_bitwise():
+    torch = gu.torch_mod()
+    lens = [37, 16, 5, 80]
+    w, x = _case("bf16_sep", 15, H=3, state=True, lengths=lens)
+    cu = x["cu_seqlens"]
+    d = gu.upload(x, True, True)
+    out, fs = gu.run_gpu(d)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        sub = {key: x[key][a:b] for key in ("q", "k", "v", "g", "beta")}
+        sub["initial_state"] = x["initial_state"][n:n + 1]
+        dn = gu.upload(sub, True, False)
+        on, fn = gu.run_gpu(dn)
+        assert torch.equal(on, out[a:b]), n
+        assert torch.equal(fn[0], fs[n]), n
+
+
+@pytest.mark.parametrize("cut", [64, 50])
+def test_split_and_resume(cut):
+    """Running [0, cut) and then [cut, T) from the carried fp32 state matches one
+    run: bitwise when the cut is on a chunk boundary, within tolerance otherwise."""
+    torch = gu.torch_mod()
+    w, x = _case("bf16_split", 16, H=2, T=160, state=True)
+    d = gu.upload(x, True, False)
+    out, fs = gu.run_gpu(d)
+    first = {key: x[key][:cut] for key in ("q", "k", "v", "g", "beta")}
+    first["initial_state"] = x["initial_state"]
+    o1, f1 = gu.run_gpu(gu.upload(first, True, False))
+    second = {key: x[key][cut:] for key in ("q", "k", "v", "g", "beta")}
+    d2 = gu.upload(second, True, False)
+    d2["initial_state"] = f1
+    o2, f2 = gu.run_gpu(d2)
+    both = torch.cat([o1, o2])
+    if cut % 16 == 0:
+        assert torch.equal(both, out) and torch.equal(f2, fs)
+    else:
+        ro, rs = gu.run_oracle(x, False)
+        gu.assert_close("out", gu.to_host(both), ro, True)
+        gu.assert_close("final_state", gu.to_host(f2), rs, True)
+
+
+def test_empty_input_copies_initial_state():
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+
+    H = 2
+    z = torch.empty((0, H, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, H, 128), dtype=torch.float32, device="cuda")
+    b = torch.empty((0, H), dtype=torch.float32, device="cuda")
+    s0 = torch.randn((1, H, 128, 128), dtype=torch.float32, device="cuda")
+    out, fs = kda.chunk_prefill(z, z, z, g, b, initial_state=s0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H, 128) and torch.equal(fs, s0)
+
+
+def test_intra_chunk_intermediates_match_chunked_reference():
+    """K1 alone: decode its per-(chunk, head) records and compare with the fp64
+    chunked form's T' = T diag(beta), M = P T', W, Q~ = Q+ - P W, K^d and gamma."""
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+    from oracle import reference
+
+    H, T = 3, 40
+    w, x = _case("intra", 21, H=H, T=T)
+    d = gu.upload(x, True, False)
+    dims = kda.make_dims(d["q"], d["v"])
+    ws = kda.workspace_for(dims, "cuda")
+    st = kda.kda_intra_chunk(d["q"].data_ptr(), d["k"].data_ptr(), d["g"].data_ptr(), d["beta"].data_ptr(),
+                             None, dims, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    n_chunks = (T + 15) // 16
+    align = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    off = align(4 * 2) + align(4 * n_chunks)
+    lane = np.arange(64)
+    cl, gl = lane & 15, lane >> 4
+    for h in range(H):
+        _, _, inter = reference.chunked(x["q"][:, h], x["k"][:, h], x["v"][:, h], x["g"][:, h],
+                                        x["beta"][:, h], None, intermediates=True)
+        for ci, it in enumerate(inter):
+            rec = raw[off + (ci * H + h) * 14848: off + (ci * H + h + 1) * 14848]
+            n = it["W"].shape[0]
+            beta_c = x["beta"][16 * ci:16 * ci + n, h].astype(np.float64)
+            tp_ref = it["T"] * beta_c[None, :]
+            m_ref = it["P"] @ tp_ref
+            qt_ref = it["Qp"] - it["P"] @ it["W"]
+
+            def bf(u16):
+                return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+            def dec_rowlayout(base):
+                a = bf(rec[base:base + 4096].view(np.uint16).reshape(4, 64, 8))
+                out = np.zeros((16, 128))
+                for s in range(4):
+                    for u in range(8):
+                        e = 8 * s + u
+                        out[cl, 16 * (e >> 2) + 4 * gl + (e & 3)] = a[s, :, u]
+                return out
+
+            def dec_tile_pairs(base):
+                a = bf(rec[base:base + 4096].view(np.uint16).reshape(4, 64, 8))
+                out = np.zeros((16, 128))
+                for mp in range(4):
+                    for u in range(8):
+                        m = 2 * mp + (u >> 2)
+                        out[4 * gl + (u & 3), 16 * m + cl] = a[mp, :, u]
+                return out
+
+            def dec_hilo(base):
+                a = bf(rec[base:base + 1024].view(np.uint16).reshape(64, 8))
+                out = np.zeros((16, 16))
+                for u in range(4):
+                    out[cl, 4 * gl + u] = a[:, u] + a[:, 4 + u]
+                return out
+
+            gam = rec[14336:14848].view(np.float32).reshape(4, 32).astype(np.float64)
+            gam_full = np.zeros(128)
+            for gg in range(4):
+                for e in range(32):
+                    gam_full[16 * (e >> 2) + 4 * gg + (e & 3)] = gam[gg, e]
+            got = {"W": dec_rowlayout(0), "QT": dec_rowlayout(4096), "KD": dec_tile_pairs(8192),
+                   "TB": dec_hilo(12288), "MM": dec_hilo(13312)}
+            ref = {"W": it["W"], "QT": qt_ref, "KD": it["Kd"], "TB": tp_ref, "MM": m_ref}
+            for key in got:
+                gv, rv = got[key], ref[key]
+                pad_rows = gv[n:]
+                assert np.all(pad_rows == 0), (key, h, ci)
+                if key in ("TB", "MM"):
+                    assert np.all(gv[:n, n:] == 0), (key, h, ci)
+                    gv, rv = gv[:n, :n], rv
+                else:
+                    gv = gv[:n]
+                max_abs, rel = gu.errors(gv, rv)
+                tol = 3e-4 if key in ("TB", "MM") else 6e-3
+                assert rel <= tol, (key, h, ci, rel, max_abs)
+            assert np.max(np.abs(gam_full / it["gamma"] - 1)) <= 2e-6
