@@ -33,6 +33,9 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the recurrent state is rescaled on the
+    # VALU every chunk, so keeping it out of AGPRs avoids copies both ways
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-I", INCLUDE,
     "-I", CSRC,

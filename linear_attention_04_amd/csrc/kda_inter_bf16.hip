@@ -6,10 +6,11 @@
 // state's value columns are independent (column j of S and of the output depends
 // only on column j of v and of the initial state), so one 64-lane wave owns 16
 // columns of one head: its 128 x 16 slice of S lives in MFMA accumulator registers
-// for the whole sequence and no wave ever waits for another.
+// for the whole sequence. A workgroup of 2 waves covers 32 columns of one head and
+// shares one copy of each chunk's operands.
 //
-// Per chunk, with S the state at the chunk start and V the chunk's 16 x 16 value
-// tile (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
+// Per chunk, with S the state at the chunk start and V the chunk's value tile
+// (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
 //   U     = T' V                      (two-term bf16 split of T'; V is exact)
 //   Delta = U - W S                   (S rounded to bf16 as the MFMA operand)
 //   O     = Q~ S + M V                -> out (bf16)
@@ -19,6 +20,13 @@
 // stores W and Q~ with matching channel order; Delta's accumulator layout is the B
 // operand of K^d^T Delta. Nothing moves across lanes except gamma, which is
 // broadcast inside 16-lane rows with DPP.
+//
+// Memory pipeline: a chunk step takes a few hundred cycles while an HBM load takes
+// on the order of a microsecond, so each workgroup keeps a ring of DEPTH chunk
+// slots in LDS that two producer waves fill with direct buffer->LDS loads
+// (buffer_load_dwordx4 ... lds) several chunks ahead; the loads hold no registers.
+// A producer waits (s_waitcnt vmcnt) for its own part of a chunk, then one
+// s_barrier per chunk publishes the slot to the compute waves.
 #include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -28,55 +36,26 @@ namespace {
 
 constexpr int KD = 128;
 constexpr int VD = 128;
-constexpr int kTiles = VD / 16;  // value-column tiles per head, one wave each
+constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
-struct ChunkOps {
-    bf16x8 w[4];
-    bf16x8 qt[4];
-    bf16x8 kd[4];
-    bf16x8 tb;
-    bf16x8 mm;
-    float2 gam;
-    uint2 v;  // V[4grp + i][16vt + c] for i = 0..3, bf16 bit patterns, two per word
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void load_ops(ChunkOps &o, const char *__restrict__ rec,
-                                         const unsigned short *__restrict__ v, int64_t tok0, int len,
-                                         int H, int h, int vt, int lane) {
-    const int c = lane & 15, grp = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        o.w[s] = *reinterpret_cast<const bf16x8 *>(rec + kRecW + (s * 64 + lane) * 16);
-        o.qt[s] = *reinterpret_cast<const bf16x8 *>(rec + kRecQT + (s * 64 + lane) * 16);
-        o.kd[s] = *reinterpret_cast<const bf16x8 *>(rec + kRecKD + (s * 64 + lane) * 16);
-    }
-    o.tb = *reinterpret_cast<const bf16x8 *>(rec + kRecTB + lane * 16);
-    o.mm = *reinterpret_cast<const bf16x8 *>(rec + kRecMM + lane * 16);
-    o.gam = *reinterpret_cast<const float2 *>(rec + kRecGAM + (grp * 32 + 2 * c) * 4);
-    unsigned int bits[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * grp + i;
-        bits[i] = r < len ? (unsigned int)v[((size_t)(tok0 + r) * H + h) * VD + 16 * vt + c] : 0u;
-    }
-    o.v.x = bits[0] | (bits[1] << 16);
-    o.v.y = bits[2] | (bits[3] << 16);
-}
-
-// {x[0..3], x[0..3]} and {x[4..7], x[4..7]}: a 4-element operand repeated over both
-// halves of the 32-long reduction of v_mfma_f32_16x16x32_bf16.
-__device__ __forceinline__ bf16x8 dup_lo(bf16x8 x) {
-    bf16x8 r;
-    r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
-    r[4] = x[0]; r[5] = x[1]; r[6] = x[2]; r[7] = x[3];
-    return r;
-}
-__device__ __forceinline__ bf16x8 dup_hi(bf16x8 x) {
-    bf16x8 r;
-    r[0] = x[4]; r[1] = x[5]; r[2] = x[6]; r[3] = x[7];
-    r[4] = x[4]; r[5] = x[5]; r[6] = x[6]; r[7] = x[7];
-    return r;
-}
+// A workgroup has kNW compute waves (16 value columns each) and kNW producer waves.
+// Producers stream each chunk into a ring slot of 16 KiB with 16 wave-wide 1 KiB
+// loads (64 lanes x 16 B), eight per producer:
+//   pieces 0..13  record bytes [0, 14336)          (W, Q~, K^d, T', M)
+//   piece 14      record bytes [14336, 14848) = gamma, lanes 32..63 load it again into [14848, 15360)
+//   piece 15      value tile [16 tokens][32 columns] bf16 at kVOff
+// Producer p issues record pieces 7p .. 7p + 6 and then piece 14 + p, so every load
+// of a producer has one role and each producer issues exactly kPerWave per chunk.
+// Only producers wait on the vector-memory counter, and they never store, so the
+// count they wait on covers their own loads alone; compute waves only read LDS,
+// compute and store.
+constexpr int kNW = 2;
+constexpr int kPerWave = 8;
+constexpr int kSlotBytes = 16384;
+constexpr int kVOff = 15360;
+static_assert(kRecGAM == 14336 && kRecBytesBf16 == 14848, "record layout");
 
 template <int M, int I>
 __device__ __forceinline__ float gamma_of(const float2 gam) {
@@ -92,11 +71,114 @@ __device__ __forceinline__ void decay_tile(f32x4 &s, const float2 gam) {
     s[3] *= gamma_of<M, 3>(gam);
 }
 
-// One chunk. Two-term products use the 32-long reduction of the MFMA as two
-// concatenated 16-long ones: [X_hi | X_lo] . [Y ; Y] = (X_hi + X_lo) Y.
-__device__ __forceinline__ void chunk_step(const ChunkOps &o, f32x4 (&S)[8], unsigned short *__restrict__ out,
-                                           int64_t tok0, int len, int H, int h, int vt, int lane) {
+// s_waitcnt vmcnt(N) without waiting on the LDS / export counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until this (producer) wave's loads for one chunk have landed: at most
+// `later` chunks' loads, issued after that chunk's, may stay outstanding. Vector
+// memory loads complete in issue order and producers issue nothing else, so the
+// count is exact. `later` is wave-uniform and in [0, DEPTH - 2].
+template <int PER_WAVE, int DEPTH>
+__device__ __forceinline__ void wait_for_chunk(int later) {
+    static_assert(DEPTH >= 2 && DEPTH <= 8, "extend the switch");
+    switch (later) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<(DEPTH > 2 ? 1 : 0) * PER_WAVE>(); break;
+    case 2: wait_vmcnt<(DEPTH > 3 ? 2 : 0) * PER_WAVE>(); break;
+    case 3: wait_vmcnt<(DEPTH > 4 ? 3 : 0) * PER_WAVE>(); break;
+    case 4: wait_vmcnt<(DEPTH > 5 ? 4 : 0) * PER_WAVE>(); break;
+    case 5: wait_vmcnt<(DEPTH > 6 ? 5 : 0) * PER_WAVE>(); break;
+    default: wait_vmcnt<(DEPTH > 7 ? 6 : 0) * PER_WAVE>(); break;
+    }
+}
+
+// Per-lane byte offsets that stay fixed for the whole sequence.
+struct LaneOffsets {
+    unsigned int rec;    // lane * 16: record pieces
+    unsigned int gam;    // (lane & 31) * 16: gamma (lanes 32..63 load it twice)
+    unsigned int v;      // value tile load of this lane: token row lane / 4, 8 columns
+    unsigned int out;    // output element (row 4grp, column col + c) within the chunk
+    unsigned int vrow;   // one token row of v / out in bytes (H * VD * 2)
+};
+
+// Buffer descriptor over `bytes` bytes at `base` (wave-uniform). Buffer accesses
+// are range-checked by the hardware: loads past the end return zero and stores
+// past the end are dropped, which is how rows past a short chunk are handled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Bytes of a chunk's rows [0, len) restricted to the workgroup's 32 columns.
+__device__ __forceinline__ int tile_bytes(int len, unsigned int vrow) {
+    return len > 0 ? (len - 1) * (int)vrow + kNW * 32 : 0;
+}
+
+// Issue producer `producer`'s share of one chunk's loads into the ring slot at LDS byte
+// offset `slot`. `rec` (the chunk's record) and `vchunk` (the chunk's first token
+// row of v at column col0) are wave-uniform; every address is a scalar base plus a
+// per-lane offset fixed for the whole sequence.
+__device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const char *rec, const char *vchunk,
+                                            int len, int producer, const LaneOffsets &lo) {
+    const __amdgpu_buffer_rsrc_t rr = rsrc(rec, kRecBytesBf16);
+#pragma unroll
+    for (int k = 0; k < kPerWave - 1; ++k) {
+        const int piece = 7 * producer + k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + piece * 1024), 16, lo.rec,
+                                                 piece * 1024, 0, 0);
+    }
+    if (producer == 0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + kRecGAM), 16, lo.gam, kRecGAM, 0,
+                                                 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vchunk, tile_bytes(len, lo.vrow));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(ring + slot + kVOff), 16, lo.v, 0, 0, 0);
+    }
+}
+
+// One chunk's operands in registers (read from its ring slot ahead of use).
+struct ChunkOps {
+    bf16x8 w[4], qt[4];
+    bf16x8 kd[8];  // K^d^T tile m repeated over both halves of the 32-long reduction
+    bf16x8 tb, mm;
+    float2 gam;
+    bf16x8 vv;     // [V; V] over the 32-long reduction
+};
+
+__device__ __forceinline__ void read_ops(ChunkOps &o, const char *slot, int wave, int lane) {
     const int c = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + (s * 64 + lane) * 16);
+        o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + (s * 64 + lane) * 16);
+    }
+    // the same 8 bytes read twice from LDS (an opaque offset keeps the two reads
+    // apart) instead of duplicating registers
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        int off = kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8;
+        const uint2 a = *reinterpret_cast<const uint2 *>(slot + off);
+        asm volatile("" : "+v"(off));
+        const uint2 b = *reinterpret_cast<const uint2 *>(slot + off);
+        o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+    }
+    o.tb = *reinterpret_cast<const bf16x8 *>(slot + kRecTB + lane * 16);
+    o.mm = *reinterpret_cast<const bf16x8 *>(slot + kRecMM + lane * 16);
+    o.gam = *reinterpret_cast<const float2 *>(slot + kRecGAM + (grp * 32 + 2 * c) * 4);
+    // rows past the end of a short chunk were loaded as zeros (range-checked loads)
+    const unsigned short *vt = reinterpret_cast<const unsigned short *>(slot + kVOff);
+    unsigned int vb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vb[i] = vt[(4 * grp + i) * (kNW * 16) + wave * 16 + c];
+    const unsigned int v01 = vb[0] | (vb[1] << 16), v23 = vb[2] | (vb[3] << 16);
+    o.vv = __builtin_bit_cast(bf16x8, make_uint4(v01, v23, v01, v23));
+}
+
+__device__ __forceinline__ void compute_chunk(const ChunkOps &o, f32x4 (&S)[8], char *ochunk, int len,
+                                              const LaneOffsets &lo) {
     bf16x8 sb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -113,10 +195,8 @@ __device__ __forceinline__ void chunk_step(const ChunkOps &o, f32x4 (&S)[8], uns
         x = mfma_16x16x32(o.w[s], sb[s], x);
         y = mfma_16x16x32(o.qt[s], sb[s], y);
     }
-    // [V; V] over the 32-long reduction (whole-vector bit cast of the packed words)
-    const bf16x8 vv = __builtin_bit_cast(bf16x8, make_uint4(o.v.x, o.v.y, o.v.x, o.v.y));
-    const f32x4 u = mfma_16x16x32(o.tb, vv, zero);  // T' V
-    y = mfma_16x16x32(o.mm, vv, y);                 // + M V
+    const f32x4 u = mfma_16x16x32(o.tb, o.vv, zero);  // T' V
+    y = mfma_16x16x32(o.mm, o.vv, y);                 // + M V
 
     // Delta = U - W S, split into bf16 hi + lo for the state update
     const f32x4 d = u - x;
@@ -136,70 +216,111 @@ __device__ __forceinline__ void chunk_step(const ChunkOps &o, f32x4 (&S)[8], uns
     decay_tile<6>(S[6], o.gam);
     decay_tile<7>(S[7], o.gam);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const bf16x8 a = (m & 1) ? dup_hi(o.kd[m >> 1]) : dup_lo(o.kd[m >> 1]);
-        S[m] = mfma_16x16x32(a, db, S[m]);  // K^d^T (Delta_hi + Delta_lo)
-    }
+    for (int m = 0; m < 8; ++m) S[m] = mfma_16x16x32(o.kd[m], db, S[m]);  // K^d^T (Delta_hi + Delta_lo)
 
+    // rows past the end of a short chunk fall outside the descriptor and are dropped
+    const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes(len, lo.vrow));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * grp + i;
-        if (r < len) {
-            const __bf16 ov = to_bf16(y[i]);
-            out[((size_t)(tok0 + r) * H + h) * VD + 16 * vt + c] = __builtin_bit_cast(unsigned short, ov);
-        }
-    }
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_bf16(y[i])), ro, lo.out,
+                                              i * lo.vrow, 0);
 }
 
-__global__ __launch_bounds__(64) void kda_inter_bf16_kernel(
+template <int DEPTH>
+__global__ __launch_bounds__(128 * kNW) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
     const char *__restrict__ records) {
-    int pair, vt;
-    xcd_unit_split(blockIdx.x, kTiles, pair, vt);
-    if (pair >= N * H) return;
+    static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
+    static_assert((DEPTH - 1) * kPerWave < 64, "a producer's loads in flight must fit the 6-bit counter");
+    extern __shared__ __attribute__((aligned(1024))) char ring[];
+    int pair, vg;
+    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
-    const int lane = threadIdx.x;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
     const int c = lane & 15, grp = lane >> 4;
+    const int col0 = vg * kNW * 16;  // first value column of the workgroup
     const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
+    const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
 
-    f32x4 S[8];
-    const size_t sbase = (size_t)pair * KD * VD + 16 * vt + c;
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[m][i] = s0 ? s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD] : 0.f;
-
-    auto span = [&](int64_t ci, int64_t &tok0, int &len) {
-        tok0 = sc.tok_begin + 16 * (ci - sc.chunk_begin);
-        const int64_t rem = sc.tok_end - tok0;
-        len = rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
+    LaneOffsets lo;
+    lo.vrow = (unsigned int)H * VD * 2;
+    lo.rec = lane * 16;
+    lo.gam = (lane & 31) * 16;
+    lo.v = (lane >> 2) * lo.vrow + (lane & 3) * 16;
+    lo.out = 4 * grp * lo.vrow + (wid * 16 + c) * 2;  // compute waves; relative to column col0
+    const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
+    const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
+    auto len_of = [&](int64_t j) {
+        const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * j);
+        return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
     };
-    auto rec_of = [&](int64_t ci) { return records + ((size_t)ci * H + h) * kRecBytesBf16; };
+    auto slot_off = [&](int64_t j) { return (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes); };
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");  // no LDS or global access moves across the barrier
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
-    ChunkOps opa, opb;
-    int64_t ci = sc.chunk_begin;
-    int64_t tok_a = 0, tok_b = 0;
-    int len_a = 0, len_b = 0;
-    if (ci < sc.chunk_end) {
-        span(ci, tok_a, len_a);
-        load_ops(opa, rec_of(ci), v, tok_a, len_a, H, h, vt, lane);
+    // Barrier B_j (j = 0 .. nchunks - 1) publishes chunk j's slot. Every wave of the
+    // workgroup passes each B_j exactly once.
+    if (wid >= kNW) {
+        // ---- producer ----
+        const int p = wid - kNW;
+        const char *rec0 = records + ((size_t)h * max_chunks + sc.chunk_begin) * kRecBytesBf16;  // head-major
+        const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
+        auto issue = [&](int64_t j) {
+            issue_chunk(ring, slot_off(j), rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows,
+                        len_of(j), p, lo);
+        };
+        for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
+        for (int64_t j = 0; j < nchunks; ++j) {
+            // chunks issued so far: 0 .. last
+            const int64_t lim = j == 0 ? DEPTH - 2 : j + DEPTH - 3;
+            const int64_t last = lim < nchunks - 1 ? lim : nchunks - 1;
+            asm volatile("" ::: "memory");
+            wait_for_chunk<kPerWave, DEPTH>((int)(last - j));
+            barrier();
+            // The slot of chunk j - 2 is free: compute waves read it before B_{j-1} and
+            // finished using it before B_j.
+            if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
+        }
+        return;
     }
-    while (ci < sc.chunk_end) {
-        if (ci + 1 < sc.chunk_end) {
-            span(ci + 1, tok_b, len_b);
-            load_ops(opb, rec_of(ci + 1), v, tok_b, len_b, H, h, vt, lane);
+
+    // ---- compute wave: 16 value columns col0 + 16 wid .. + 15 ----
+    f32x4 S[8];
+    const size_t sbase = (size_t)pair * KD * VD + col0 + wid * 16 + c;
+    if (s0) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    char *o0 = reinterpret_cast<char *>(out) + tok_bytes;
+
+    // Software pipeline: chunk j + 1's operands are read from LDS while chunk j is computed.
+    auto step = [&](int64_t j, const ChunkOps &cur, ChunkOps &next) {
+        if (j + 1 < nchunks) {
+            barrier();  // B_{j+1}
+            read_ops(next, ring + slot_off(j + 1), wid, lane);
         }
-        chunk_step(opa, S, out, tok_a, len_a, H, h, vt, lane);
-        if (++ci >= sc.chunk_end) break;
-        if (ci + 1 < sc.chunk_end) {
-            span(ci + 1, tok_a, len_a);
-            load_ops(opa, rec_of(ci + 1), v, tok_a, len_a, H, h, vt, lane);
-        }
-        chunk_step(opb, S, out, tok_b, len_b, H, h, vt, lane);
-        ++ci;
+        compute_chunk(cur, S, o0 + (size_t)j * chunk_rows, len_of(j), lo);
+    };
+    ChunkOps opa, opb;
+    if (nchunks > 0) {
+        barrier();  // B_0
+        read_ops(opa, ring + slot_off(0), wid, lane);
+    }
+    for (int64_t j = 0; j < nchunks; j += 2) {
+        step(j, opa, opb);
+        if (j + 1 < nchunks) step(j + 1, opb, opa);
     }
 
     if (sT) {
@@ -211,19 +332,35 @@ __global__ __launch_bounds__(64) void kda_inter_bf16_kernel(
     }
 }
 
+template <int DEPTH>
+hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
+                  const Geometry &geo, const void *ws, hipStream_t stream) {
+    const int pairs = geo.N * geo.H;
+    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / kNW);
+    const char *base = static_cast<const char *>(ws);
+    const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
+    const size_t lds = (size_t)DEPTH * kSlotBytes;
+    auto kern = kda_inter_bf16_kernel<DEPTH>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(128 * kNW), lds, stream, static_cast<const unsigned short *>(v),
+                       cu_seqlens, chunk_off, s0, static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N,
+                       geo.max_chunks, base + geo.off_records);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream) {
-    const int pairs = geo.N * geo.H;
-    const int blocks = ((pairs + 7) / 8) * 8 * kTiles;
-    const char *base = static_cast<const char *>(ws);
-    const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    hipLaunchKernelGGL(kda_inter_bf16_kernel, dim3(blocks), dim3(64), 0, stream,
-                       static_cast<const unsigned short *>(v), cu_seqlens, chunk_off, s0,
-                       static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks,
-                       base + geo.off_records);
-    return hipGetLastError();
+    // One workgroup (2 compute + 2 producer waves) per 32 value columns of a
+    // (sequence, head). With at most one workgroup per CU the ring is 8 chunks deep
+    // (128 KiB of LDS); beyond that it is 4 deep so that two workgroups fit on a CU.
+    constexpr int kCUs = 256;
+    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
+    if (blocks <= kCUs) return launch<8>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch<4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 }  // namespace kda

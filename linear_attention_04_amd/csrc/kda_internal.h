@@ -36,7 +36,7 @@ struct Geometry {
     int64_t max_chunks;      // upper bound on chunks over all sequences
     size_t off_chunk_off;    // int32 [N + 1]
     size_t off_chunk_seq;    // int32 [max_chunks]
-    size_t off_records;      // records [max_chunks][H]
+    size_t off_records;      // records [H][max_chunks] (head-major: a head's chunks are contiguous)
     size_t record_bytes;
     size_t total_bytes;
 };

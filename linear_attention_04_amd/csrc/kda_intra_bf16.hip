@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     }
 
     if (!head_ok) return;
-    char *rec = records + ((size_t)chunk * H + h) * kRecBytesBf16;
+    char *rec = records + ((size_t)h * max_chunks + chunk) * kRecBytesBf16;  // head-major
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         *reinterpret_cast<bf16x8 *>(rec + kRecW + (s * 64 + lane) * 16) = wv[s];
