@@ -19,6 +19,7 @@ namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -42,12 +43,30 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
     return r;
 }
 
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): ~16 significant bits in two bf16 parts.
+// Two fp32 values rounded to a packed bf16 pair (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+    bf16x2 p;
+    p[0] = to_bf16(a);
+    p[1] = to_bf16(b);
+    return __builtin_bit_cast(unsigned int, p);
+}
+
+// (a, b) = hi + lo with hi = bf16(a, b), lo = bf16((a, b) - hi): ~16 significant
+// bits in two packed bf16 pairs, three VALU operations per value.
+__device__ __forceinline__ void split_pair(float a, float b, unsigned int &hi, unsigned int &lo) {
+    unsigned int h = pack_bf16x2(a, b);
+    asm volatile("" : "+v"(h));  // reuse the packed word for both halves (no second conversion)
+    hi = h;
+    lo = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
+// x = hi + lo for four values.
 __device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = to_bf16(x[i]);
-        lo[i] = to_bf16(x[i] - from_bf16(hi[i]));
-    }
+    uint2 h, l;
+    split_pair(x[0], x[1], h.x, l.x);
+    split_pair(x[2], x[3], h.y, l.y);
+    hi = __builtin_bit_cast(bf16x4, h);
+    lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // DPP: value of lane (l - N) within the same 16-lane row, or 0 where that lane is

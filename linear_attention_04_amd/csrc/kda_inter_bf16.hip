@@ -101,7 +101,7 @@ struct LaneOffsets {
     unsigned int rec;    // lane * 16: record pieces
     unsigned int gam;    // (lane & 31) * 16: gamma (lanes 32..63 load it twice)
     unsigned int v;      // value tile load of this lane: token row lane / 4, 8 columns
-    unsigned int out;    // output element (row 4grp, column col + c) within the chunk
+    unsigned int out;    // output: token c, columns col + 4grp .. + 3, within the chunk
     unsigned int vrow;   // one token row of v / out in bytes (H * VD * 2)
 };
 
@@ -188,15 +188,19 @@ __device__ __forceinline__ void compute_chunk(const ChunkOps &o, f32x4 (&S)[8], 
             sb[s][4 + i] = to_bf16(S[2 * s + 1][i]);
         }
     }
+    // The output is formed transposed, O^T = S^T Q~^T + V^T M^T, by swapping the
+    // operands: 16x16x32 operand layouts are symmetric (lane l: row / column l % 16,
+    // eight reduction elements), so the same registers serve. Each lane then holds
+    // four consecutive value columns of one token and stores them at once.
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 x = zero, y = zero;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         x = mfma_16x16x32(o.w[s], sb[s], x);
-        y = mfma_16x16x32(o.qt[s], sb[s], y);
+        y = mfma_16x16x32(sb[s], o.qt[s], y);
     }
     const f32x4 u = mfma_16x16x32(o.tb, o.vv, zero);  // T' V
-    y = mfma_16x16x32(o.mm, o.vv, y);                 // + M V
+    y = mfma_16x16x32(o.vv, o.mm, y);                 // + (M V)^T
 
     // Delta = U - W S, split into bf16 hi + lo for the state update
     const f32x4 d = u - x;
@@ -218,12 +222,12 @@ __device__ __forceinline__ void compute_chunk(const ChunkOps &o, f32x4 (&S)[8], 
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = mfma_16x16x32(o.kd[m], db, S[m]);  // K^d^T (Delta_hi + Delta_lo)
 
-    // rows past the end of a short chunk fall outside the descriptor and are dropped
+    // y[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
+    // end of a short chunk fall outside the descriptor and are dropped
     const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes(len, lo.vrow));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_bf16(y[i])), ro, lo.out,
-                                              i * lo.vrow, 0);
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
 }
 
 template <int DEPTH>
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(128 * kNW) void kda_inter_bf16_kernel(
     lo.rec = lane * 16;
     lo.gam = (lane & 31) * 16;
     lo.v = (lane >> 2) * lo.vrow + (lane & 3) * 16;
-    lo.out = 4 * grp * lo.vrow + (wid * 16 + c) * 2;  // compute waves; relative to column col0
+    lo.out = c * lo.vrow + (wid * 16 + 4 * grp) * 2;  // compute waves: token c, columns 4grp..+3 (from col0)
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
     auto len_of = [&](int64_t j) {

@@ -96,28 +96,39 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     for (int e = 0; e < 32; ++e) gr[e] = row_inclusive_sum(gr[e]);
     float *G = gr;
 
-    // ---- A and P on the MFMA: two-term bf16 splits of both factors ----
+    // ---- A and P on the MFMA: two-term bf16 splits of both factors. Gate factors
+    // up = exp(G - G_ref), dn = exp(G_ref - G) with G_ref the running gate at token 7;
+    // K^d = k exp(G_C - G) = k dn exp(G_C - G_ref) goes to LDS right away. ----
     f32x4 acc_a = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        bf16x8 khh, khl, kbh, kbl, qhh, qhl;
+        unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = 8 * s + u;
-            const float d = G[e] - row_bcast<7>(G[e]);
-            const float up = __expf(d), dn = __expf(-d);
-            const float kh = kr[e] * up, qh = qr[e] * up, kb = kr[e] * dn;
-            khh[u] = to_bf16(kh); khl[u] = to_bf16(kh - from_bf16(khh[u]));
-            qhh[u] = to_bf16(qh); qhl[u] = to_bf16(qh - from_bf16(qhh[u]));
-            kbh[u] = to_bf16(kb); kbl[u] = to_bf16(kb - from_bf16(kbh[u]));
+        for (int u = 0; u < 4; ++u) {
+            const int e = 8 * s + 2 * u;
+            const float d0 = G[e] - row_bcast<7>(G[e]), d1 = G[e + 1] - row_bcast<7>(G[e + 1]);
+            const float up0 = __expf(d0), up1 = __expf(d1);
+            const float dn0 = __expf(-d0), dn1 = __expf(-d1);
+            const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);  // channel of e; e + 1 is ch + 1
+            L.kd[ch * kChStride + c] = to_bf16(kr[e] * (dn0 * row_bcast<15>(up0)));
+            L.kd[(ch + 1) * kChStride + c] = to_bf16(kr[e + 1] * (dn1 * row_bcast<15>(up1)));
+            split_pair(kr[e] * up0, kr[e + 1] * up1, khh[u], khl[u]);
+            split_pair(qr[e] * up0, qr[e + 1] * up1, qhh[u], qhl[u]);
+            split_pair(kr[e] * dn0, kr[e + 1] * dn1, kbh[u], kbl[u]);
         }
-        acc_a = mfma_16x16x32(khh, kbh, acc_a);
-        acc_a = mfma_16x16x32(khl, kbh, acc_a);
-        acc_a = mfma_16x16x32(khh, kbl, acc_a);
-        acc_p = mfma_16x16x32(qhh, kbh, acc_p);
-        acc_p = mfma_16x16x32(qhl, kbh, acc_p);
-        acc_p = mfma_16x16x32(qhh, kbl, acc_p);
+        const bf16x8 vkhh = __builtin_bit_cast(bf16x8, make_uint4(khh[0], khh[1], khh[2], khh[3]));
+        const bf16x8 vkhl = __builtin_bit_cast(bf16x8, make_uint4(khl[0], khl[1], khl[2], khl[3]));
+        const bf16x8 vkbh = __builtin_bit_cast(bf16x8, make_uint4(kbh[0], kbh[1], kbh[2], kbh[3]));
+        const bf16x8 vkbl = __builtin_bit_cast(bf16x8, make_uint4(kbl[0], kbl[1], kbl[2], kbl[3]));
+        const bf16x8 vqhh = __builtin_bit_cast(bf16x8, make_uint4(qhh[0], qhh[1], qhh[2], qhh[3]));
+        const bf16x8 vqhl = __builtin_bit_cast(bf16x8, make_uint4(qhl[0], qhl[1], qhl[2], qhl[3]));
+        acc_a = mfma_16x16x32(vkhh, vkbh, acc_a);
+        acc_a = mfma_16x16x32(vkhl, vkbh, acc_a);
+        acc_a = mfma_16x16x32(vkhh, vkbl, acc_a);
+        acc_p = mfma_16x16x32(vqhh, vkbh, acc_p);
+        acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
+        acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
     }
 
     if (grp == 0) L.beta[c] = b;
@@ -147,16 +158,16 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
         L.tb[(4 * grp + i) * 16 + c] = xi * b;
     }
 
-    // ---- K+ and K^d, channel-major in LDS for the transposed operands; Q+ in place ----
+    // ---- K+ channel-major in LDS for the transposed operand; Q+ in place; gamma =
+    // exp(G_C) is token 15's exp(G), broadcast ----
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
         const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);
-        const float gc = row_bcast<15>(G[e]);
         const float ep = __expf(G[e]);
         L.kp[ch * kChStride + c] = kr[e] * ep;
-        L.kd[ch * kChStride + c] = to_bf16(kr[e] * __expf(gc - G[e]));
         qr[e] *= ep;
-        if (c == 0) L.gam[ch] = __expf(gc);
+        const float gam = row_bcast<15>(ep);
+        if (c == 0) L.gam[ch] = gam;
     }
     const float *qp = qr;
     __syncthreads();
