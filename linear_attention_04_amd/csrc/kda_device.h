@@ -76,10 +76,12 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
 }
 
-// DPP: value of lane N of this lane's 16-lane row.
+// DPP: value of lane N of this lane's 16-lane row. Every source lane exists, so
+// bound_ctrl (zero for a missing source) changes nothing here; it lets the compiler
+// fold the move into the instruction that uses it.
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, true));
 }
 
 // Inclusive prefix sum over the 16 lanes of each row (lane c gets x_0 + ... + x_c).

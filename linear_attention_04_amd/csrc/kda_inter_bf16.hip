@@ -4,10 +4,11 @@
 // low-parallelism half of the two-kernel split (augursoft.site
 // "Kimi K3 的三個系統設計", section "為什麼 FlashKDA 選擇 16-token chunks"). The
 // state's value columns are independent (column j of S and of the output depends
-// only on column j of v and of the initial state), so one 64-lane wave owns 16
-// columns of one head: its 128 x 16 slice of S lives in MFMA accumulator registers
-// for the whole sequence. A workgroup of 2 waves covers 32 columns of one head and
-// shares one copy of each chunk's operands.
+// only on column j of v and of the initial state), so a workgroup owns 32 columns
+// of one head, as two 16-column tiles, and shares one copy of each chunk's operands
+// between them. Each tile's 128 x 16 slice of S lives in MFMA accumulator registers
+// for the whole sequence, split by rows over two waves (see the compute waves below),
+// so that every SIMD of the CU runs one link of a recurrence chain.
 //
 // Per chunk, with S the state at the chunk start and V the chunk's value tile
 // (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
@@ -18,15 +19,16 @@
 // The accumulator layout of S (lane: rows 4grp + i of column c) is, after rounding
 // to bf16, directly the B operand of W S and Q~ S, because the intra-chunk kernel
 // stores W and Q~ with matching channel order; Delta's accumulator layout is the B
-// operand of K^d^T Delta. Nothing moves across lanes except gamma, which is
-// broadcast inside 16-lane rows with DPP.
+// operand of K^d^T Delta. Across lanes, only gamma moves (DPP broadcasts inside
+// 16-lane rows); across waves, only the partial W S and Q~ S (through LDS).
 //
 // Memory pipeline: a chunk step takes a few hundred cycles while an HBM load takes
 // on the order of a microsecond, so each workgroup keeps a ring of DEPTH chunk
 // slots in LDS that two producer waves fill with direct buffer->LDS loads
 // (buffer_load_dwordx4 ... lds) several chunks ahead; the loads hold no registers.
 // A producer waits (s_waitcnt vmcnt) for its own part of a chunk, then one
-// s_barrier per chunk publishes the slot to the compute waves.
+// s_barrier per chunk publishes the slot to the compute waves (and, at the same
+// time, the previous chunk's partial products between the two halves of a tile).
 #include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -40,9 +42,9 @@ constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// A workgroup has kNW compute waves (16 value columns each) and kNW producer waves.
-// Producers stream each chunk into a ring slot of 16 KiB with 16 wave-wide 1 KiB
-// loads (64 lanes x 16 B), eight per producer:
+// A workgroup has 2 kNW compute waves (kNW tiles of 16 value columns, two waves
+// each) and kNW producer waves. Producers stream each chunk into a ring slot of
+// 16 KiB with 16 wave-wide 1 KiB loads (64 lanes x 16 B), eight per producer:
 //   pieces 0..13  record bytes [0, 14336)          (W, Q~, K^d, T', M)
 //   piece 14      record bytes [14336, 14848) = gamma, lanes 32..63 load it again into [14848, 15360)
 //   piece 15      value tile [16 tokens][32 columns] bf16 at kVOff
@@ -139,49 +141,72 @@ __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const
     }
 }
 
-// One chunk's operands in registers (read from its ring slot ahead of use).
-struct ChunkOps {
-    bf16x8 w[4], qt[4];
-    bf16x8 kd[8];  // K^d^T tile m repeated over both halves of the 32-long reduction
-    bf16x8 tb, mm;
+// Compute waves: kNW value tiles x 2 halves of the key dimension. Compute wave
+// (vt, kh) holds rows 64 kh .. 64 kh + 63 of tile vt's 128 x 16 state slice, i.e. the
+// four 16 x 16 accumulator tiles M = 4 kh .. 4 kh + 3. W S, Q~ S and K^d^T Delta all
+// split along those rows, so each chunk costs a wave half the MFMA and VALU work of
+// the whole slice; the two halves of a tile swap their partial W S through LDS at
+// the chunk barrier, and half 1 hands half 0 its partial Q~ S for the output.
+constexpr int kHalves = 2;
+constexpr int kComputeWaves = kNW * kHalves;
+constexpr int kWaves = kComputeWaves + kNW;  // compute waves, then producers
+
+// Exchange area after the ring: [chunk parity][tile][slot][64 lanes] f32x4 with
+// slot 0 = half 0's W S part, slot 1 = half 1's W S part minus T' V, slot 2 = half
+// 1's Q~ S part (transposed output layout).
+constexpr int kXchgSlots = 3;
+constexpr int kXchgBytes = 2 * kNW * kXchgSlots * 1024;
+
+// One chunk's operands for one half, in registers (read from the ring slot ahead of use).
+struct HalfOps {
+    bf16x8 w[2], qt[2];  // slabs 2 kh, 2 kh + 1 of W and Q~
+    bf16x8 kd[4];        // K^d^T tiles 4 kh .. 4 kh + 3, each over both halves of the 32-long reduction
+    bf16x8 tv;           // half 0: M (hi | lo), for M V; half 1: T' (hi | lo), for T' V
     float2 gam;
-    bf16x8 vv;     // [V; V] over the 32-long reduction
+    bf16x8 vv;           // [V; V] over the 32-long reduction
 };
 
-__device__ __forceinline__ void read_ops(ChunkOps &o, const char *slot, int wave, int lane) {
+template <int KH>
+__device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, int lane) {
     const int c = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + (s * 64 + lane) * 16);
-        o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + (s * 64 + lane) * 16);
+    for (int s = 0; s < 2; ++s) {
+        o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + ((2 * KH + s) * 64 + lane) * 16);
+        o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + ((2 * KH + s) * 64 + lane) * 16);
     }
     // the same 8 bytes read twice from LDS (an opaque offset keeps the two reads
     // apart) instead of duplicating registers
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int mm = 0; mm < 4; ++mm) {
+        const int m = 4 * KH + mm;
         int off = kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8;
         const uint2 a = *reinterpret_cast<const uint2 *>(slot + off);
         asm volatile("" : "+v"(off));
         const uint2 b = *reinterpret_cast<const uint2 *>(slot + off);
-        o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+        o.kd[mm] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
     }
-    o.tb = *reinterpret_cast<const bf16x8 *>(slot + kRecTB + lane * 16);
-    o.mm = *reinterpret_cast<const bf16x8 *>(slot + kRecMM + lane * 16);
+    o.tv = *reinterpret_cast<const bf16x8 *>(slot + (KH ? kRecTB : kRecMM) + lane * 16);
     o.gam = *reinterpret_cast<const float2 *>(slot + kRecGAM + (grp * 32 + 2 * c) * 4);
     // rows past the end of a short chunk were loaded as zeros (range-checked loads)
-    const unsigned short *vt = reinterpret_cast<const unsigned short *>(slot + kVOff);
+    const unsigned short *vt16 = reinterpret_cast<const unsigned short *>(slot + kVOff);
     unsigned int vb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vb[i] = vt[(4 * grp + i) * (kNW * 16) + wave * 16 + c];
+    for (int i = 0; i < 4; ++i) vb[i] = vt16[(4 * grp + i) * (kNW * 16) + vt * 16 + c];
     const unsigned int v01 = vb[0] | (vb[1] << 16), v23 = vb[2] | (vb[3] << 16);
     o.vv = __builtin_bit_cast(bf16x8, make_uint4(v01, v23, v01, v23));
 }
 
-__device__ __forceinline__ void compute_chunk(const ChunkOps &o, f32x4 (&S)[8], char *ochunk, int len,
-                                              const LaneOffsets &lo) {
-    bf16x8 sb[4];
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// First half of a chunk step, before the barrier: partial W S and Q~ S over this
+// wave's rows, published to the partner; then the decay of this wave's rows.
+template <int KH>
+__device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f32x4 &x, f32x4 &y,
+                                             char *xchg, int lane) {
+    bf16x8 sb[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sb[s][i] = to_bf16(S[2 * s][i]);
@@ -191,47 +216,115 @@ __device__ __forceinline__ void compute_chunk(const ChunkOps &o, f32x4 (&S)[8], 
     // The output is formed transposed, O^T = S^T Q~^T + V^T M^T, by swapping the
     // operands: 16x16x32 operand layouts are symmetric (lane l: row / column l % 16,
     // eight reduction elements), so the same registers serve. Each lane then holds
-    // four consecutive value columns of one token and stores them at once.
+    // four consecutive value columns of one token.
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 x = zero, y = zero;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        x = mfma_16x16x32(o.w[s], sb[s], x);
-        y = mfma_16x16x32(sb[s], o.qt[s], y);
+    x = mfma_16x16x32(o.w[0], sb[0], zero);
+    y = mfma_16x16x32(sb[0], o.qt[0], zero);
+    x = mfma_16x16x32(o.w[1], sb[1], x);
+    y = mfma_16x16x32(sb[1], o.qt[1], y);
+    if (KH == 0) {
+        *reinterpret_cast<f32x4 *>(xchg + lane * 16) = x;
+        y = mfma_16x16x32(o.vv, o.tv, y);  // + (M V)^T
+    } else {
+        x -= mfma_16x16x32(o.tv, o.vv, zero);  // - T' V
+        *reinterpret_cast<f32x4 *>(xchg + 1024 + lane * 16) = x;
+        *reinterpret_cast<f32x4 *>(xchg + 2048 + lane * 16) = y;
     }
-    const f32x4 u = mfma_16x16x32(o.tb, o.vv, zero);  // T' V
-    y = mfma_16x16x32(o.vv, o.mm, y);                 // + (M V)^T
+    decay_tile<4 * KH + 0>(S[0], o.gam);
+    decay_tile<4 * KH + 1>(S[1], o.gam);
+    decay_tile<4 * KH + 2>(S[2], o.gam);
+    decay_tile<4 * KH + 3>(S[3], o.gam);
+}
 
-    // Delta = U - W S, split into bf16 hi + lo for the state update
-    const f32x4 d = u - x;
+// The partner half's contribution for chunk parity buffer `xchg`: half 0 takes
+// half 1's W S part (minus T' V) and output part; half 1 takes half 0's W S part.
+template <int KH>
+__device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &px, f32x4 &py) {
+    if (KH == 0) {
+        px = *reinterpret_cast<const f32x4 *>(xchg + 1024 + lane * 16);
+        py = *reinterpret_cast<const f32x4 *>(xchg + 2048 + lane * 16);
+    } else {
+        px = *reinterpret_cast<const f32x4 *>(xchg + lane * 16);
+    }
+}
+
+// Second half, after the barrier: Delta = T' V - W S from both parts (the two
+// halves form the same sum, so they hold bitwise equal Delta), the state update of
+// this wave's rows and, on half 0, the output.
+template <int KH>
+__device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], const f32x4 &x, const f32x4 &y,
+                                             const f32x4 &px, const f32x4 &py, char *ochunk, int len,
+                                             const LaneOffsets &lo) {
+    const f32x4 x0 = KH == 0 ? x : px;
+    const f32x4 z1 = KH == 0 ? px : x;
+    const f32x4 d = -(x0 + z1);
     bf16x8 db;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         db[i] = to_bf16(d[i]);
         db[4 + i] = to_bf16(d[i] - from_bf16(db[i]));
     }
-
-    decay_tile<0>(S[0], o.gam);
-    decay_tile<1>(S[1], o.gam);
-    decay_tile<2>(S[2], o.gam);
-    decay_tile<3>(S[3], o.gam);
-    decay_tile<4>(S[4], o.gam);
-    decay_tile<5>(S[5], o.gam);
-    decay_tile<6>(S[6], o.gam);
-    decay_tile<7>(S[7], o.gam);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) S[m] = mfma_16x16x32(o.kd[m], db, S[m]);  // K^d^T (Delta_hi + Delta_lo)
+    for (int mm = 0; mm < 4; ++mm) S[mm] = mfma_16x16x32(o.kd[mm], db, S[mm]);  // K^d^T (Delta_hi + Delta_lo)
+    if (KH == 0) {
+        const f32x4 yt = y + py;
+        // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
+        // end of a short chunk fall outside the descriptor and are dropped
+        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes(len, lo.vrow));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 packed = {pack_bf16x2(yt[0], yt[1]), pack_bf16x2(yt[2], yt[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+    }
+}
 
-    // y[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
-    // end of a short chunk fall outside the descriptor and are dropped
-    const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes(len, lo.vrow));
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");  // no LDS or global access moves across the barrier
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The chunk loop of compute wave (vt, KH). Barrier B_j (j = 0 .. nchunks) is passed
+// once by every wave of the workgroup: B_j (j < nchunks) publishes chunk j's ring
+// slot, and B_{j+1} also publishes the partial products of chunk j.
+template <int KH, int DEPTH>
+__device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
+                                             char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo) {
+    auto slot_of = [&](int64_t j) {
+        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+    };
+    auto xchg_of = [&](int64_t j) {
+        return ring + DEPTH * kSlotBytes + (((int)(j & 1) * kNW + vt) * kXchgSlots) * 1024;
+    };
+    auto len_of = [&](int64_t j) {
+        const int64_t rem = tok_rows - 16 * j;
+        return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
+    };
+    // Every step reads the next slot, also after the last chunk: that read lands in
+    // LDS the workgroup owns and its values are never used, and it keeps the loop
+    // body free of branches.
+    auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
+        f32x4 x, y, px, py;
+        char *xc = xchg_of(j);
+        chunk_part_a<KH>(cur, S, x, y, xc, lane);
+        wait_lgkm0();  // the partial products are in LDS before the barrier
+        barrier();     // B_{j+1}
+        read_partner<KH>(xc, lane, px, py);
+        read_ops<KH>(next, slot_of(j + 1), vt, lane);
+        chunk_part_b<KH>(cur, S, x, y, px, py, o0 + (size_t)j * chunk_rows, len_of(j), lo);
+    };
+    HalfOps opa, opb;
+    barrier();  // B_0
+    read_ops<KH>(opa, slot_of(0), vt, lane);
+    int64_t j = 0;
+    for (; j + 2 <= nchunks; j += 2) {
+        step(j, opa, opb);
+        step(j + 1, opb, opa);
+    }
+    if (j < nchunks) step(j, opa, opb);
 }
 
 template <int DEPTH>
-__global__ __launch_bounds__(128 * kNW) void kda_inter_bf16_kernel(
+__global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
@@ -255,30 +348,21 @@ __global__ __launch_bounds__(128 * kNW) void kda_inter_bf16_kernel(
     lo.rec = lane * 16;
     lo.gam = (lane & 31) * 16;
     lo.v = (lane >> 2) * lo.vrow + (lane & 3) * 16;
-    lo.out = c * lo.vrow + (wid * 16 + 4 * grp) * 2;  // compute waves: token c, columns 4grp..+3 (from col0)
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
-    auto len_of = [&](int64_t j) {
-        const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * j);
-        return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
-    };
-    auto slot_off = [&](int64_t j) { return (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes); };
-    auto barrier = [&]() {
-        asm volatile("" ::: "memory");  // no LDS or global access moves across the barrier
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
 
-    // Barrier B_j (j = 0 .. nchunks - 1) publishes chunk j's slot. Every wave of the
-    // workgroup passes each B_j exactly once.
-    if (wid >= kNW) {
+    if (wid >= kComputeWaves) {
         // ---- producer ----
-        const int p = wid - kNW;
+        const int p = wid - kComputeWaves;
         const char *rec0 = records + ((size_t)h * max_chunks + sc.chunk_begin) * kRecBytesBf16;  // head-major
         const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
+        auto len_of = [&](int64_t j) {
+            const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * j);
+            return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
+        };
         auto issue = [&](int64_t j) {
-            issue_chunk(ring, slot_off(j), rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows,
-                        len_of(j), p, lo);
+            const unsigned int slot = (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+            issue_chunk(ring, slot, rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows, len_of(j), p, lo);
         };
         for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
         for (int64_t j = 0; j < nchunks; ++j) {
@@ -287,52 +371,45 @@ __global__ __launch_bounds__(128 * kNW) void kda_inter_bf16_kernel(
             const int64_t last = lim < nchunks - 1 ? lim : nchunks - 1;
             asm volatile("" ::: "memory");
             wait_for_chunk<kPerWave, DEPTH>((int)(last - j));
-            barrier();
-            // The slot of chunk j - 2 is free: compute waves read it before B_{j-1} and
-            // finished using it before B_j.
+            barrier();  // B_j
+            // The slot of chunk j - 2 is free: compute waves read it after B_{j-2}
+            // and consumed what they read before B_{j-1}.
             if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
         }
+        barrier();  // B_nchunks
         return;
     }
 
-    // ---- compute wave: 16 value columns col0 + 16 wid .. + 15 ----
-    f32x4 S[8];
-    const size_t sbase = (size_t)pair * KD * VD + col0 + wid * 16 + c;
+    // ---- compute wave (vt, kh): value columns col0 + 16 vt .. + 15, rows 64 kh .. + 63 ----
+    const int vt = wid >> 1, kh = wid & 1;
+    lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
+    f32x4 S[4];
+    const size_t sbase = (size_t)pair * KD * VD + (size_t)(64 * kh) * VD + col0 + vt * 16 + c;
     if (s0) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
     } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // Settle the state loads here: otherwise the counter wait that guards S's first
+    // use sits inside the chunk loop and, since stores count on the same counter,
+    // makes every chunk wait for the previous chunk's output store to complete.
+    wait_vmcnt<0>();
     char *o0 = reinterpret_cast<char *>(out) + tok_bytes;
-
-    // Software pipeline: chunk j + 1's operands are read from LDS while chunk j is computed.
-    auto step = [&](int64_t j, const ChunkOps &cur, ChunkOps &next) {
-        if (j + 1 < nchunks) {
-            barrier();  // B_{j+1}
-            read_ops(next, ring + slot_off(j + 1), wid, lane);
-        }
-        compute_chunk(cur, S, o0 + (size_t)j * chunk_rows, len_of(j), lo);
-    };
-    ChunkOps opa, opb;
-    if (nchunks > 0) {
-        barrier();  // B_0
-        read_ops(opa, ring + slot_off(0), wid, lane);
-    }
-    for (int64_t j = 0; j < nchunks; j += 2) {
-        step(j, opa, opb);
-        if (j + 1 < nchunks) step(j + 1, opb, opa);
-    }
+    const int64_t tok_rows = sc.tok_end - sc.tok_begin;
+    if (kh == 0)
+        compute_wave<0, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
+    else
+        compute_wave<1, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
 
     if (sT) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
+            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
     }
 }
 
@@ -343,12 +420,12 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / kNW);
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    const size_t lds = (size_t)DEPTH * kSlotBytes;
+    const size_t lds = (size_t)DEPTH * kSlotBytes + kXchgBytes;
     auto kern = kda_inter_bf16_kernel<DEPTH>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(128 * kNW), lds, stream, static_cast<const unsigned short *>(v),
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kWaves), lds, stream, static_cast<const unsigned short *>(v),
                        cu_seqlens, chunk_off, s0, static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N,
                        geo.max_chunks, base + geo.off_records);
     return hipGetLastError();
@@ -358,9 +435,10 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
 
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream) {
-    // One workgroup (2 compute + 2 producer waves) per 32 value columns of a
+    // One workgroup (4 compute + 2 producer waves) per 32 value columns of a
     // (sequence, head). With at most one workgroup per CU the ring is 8 chunks deep
-    // (128 KiB of LDS); beyond that it is 4 deep so that two workgroups fit on a CU.
+    // (128 KiB of LDS + 12 KiB exchange); beyond that it is 4 deep so that two
+    // workgroups fit on a CU.
     constexpr int kCUs = 256;
     const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
     if (blocks <= kCUs) return launch<8>(v, cu_seqlens, s0, out, sT, geo, ws, stream);

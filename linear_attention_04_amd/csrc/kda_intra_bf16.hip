@@ -61,8 +61,12 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;
     const int grp = lane >> 4;
-    const int64_t chunk = blockIdx.x;
-    const int h_raw = blockIdx.y * kWaves + wave;
+    // Head groups vary fastest over the linear workgroup id, so the workgroups in
+    // flight together read all heads of a contiguous token range (one sequential
+    // stream per input tensor) instead of a narrow strided column of it.
+    const int head_groups = (H + kWaves - 1) / kWaves;
+    const int64_t chunk = blockIdx.x / head_groups;
+    const int h_raw = (int)(blockIdx.x - chunk * head_groups) * kWaves + wave;
     const bool head_ok = h_raw < H;
     const int h = head_ok ? h_raw : H - 1;
 
@@ -256,7 +260,9 @@ hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const
     char *base = static_cast<char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     const int32_t *chunk_seq = reinterpret_cast<const int32_t *>(base + geo.off_chunk_seq);
-    const dim3 grid((unsigned)geo.max_chunks, (unsigned)((geo.H + kWaves - 1) / kWaves));
+    const int64_t blocks = geo.max_chunks * ((geo.H + kWaves - 1) / kWaves);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
     hipLaunchKernelGGL(kda_intra_bf16_kernel, grid, dim3(64 * kWaves), 0, stream,
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), g, beta,
                        cu_seqlens, chunk_off, chunk_seq, geo.T, geo.H, geo.N, geo.max_chunks,
