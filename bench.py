@@ -21,16 +21,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 WORKLOAD = "fixed_h64_t8192"
+SCALAR_GATE_WORKLOAD = "fixed_h64_t8192_scalar_gate"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Algorithmic bytes per (token, head) of each kernel at K = V = 128 (bf16 io):
-#  intra: reads q, k (bf16) + g (fp32) + beta = 2*128 + 2*128 + 4*128 + 4 = 1028,
+#  intra: reads q, k (bf16) + g (fp32) + beta = 2*128 + 2*128 + 4*128 + 4 = 1028
+#         (520 with a scalar gate: g is one fp32 per token and head),
 #         writes its per-chunk record 14848 B / 16 tokens = 928;
 #  inter: reads the record (928) and v (256), writes out (256), plus the fp32
 #         final state (and initial state, if any) per (sequence, head).
-INTRA_BYTES_PER_TH = 1028 + 928
+INTRA_BYTES_PER_TH = {"channel": 1028 + 928, "scalar": 520 + 928}
 INTER_BYTES_PER_TH = 928 + 256 + 256
 STATE_BYTES = 128 * 128 * 4
 
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--gate", choices=("channel", "scalar"), default="channel",
+                    help="scalar: the same shape with one gate per token and head (Gated DeltaNet)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM counters)")
     return ap.parse_args()
@@ -68,10 +72,10 @@ def source_digest(names):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, digest: str, launches_units: float):
+def traffic_for(kernel: str, digest: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken on
     the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_{WORKLOAD}.json")
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -123,7 +127,10 @@ def main():
     if args.copy_calibration:
         return copy_calibration()
     kda.load_library()
-    w = inputs.WORKLOADS[WORKLOAD]
+    if args.gate == "scalar":
+        w = inputs.custom_workload(SCALAR_GATE_WORKLOAD, 1, 64, 8192, gate="scalar")
+    else:
+        w = inputs.WORKLOADS[WORKLOAD]
     x = inputs.generate(w)
     dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
                          if bf else torch.from_numpy(a).to("cuda"))
@@ -132,7 +139,7 @@ def main():
     T, H = w.total_tokens, w.heads
     out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
     fs = torch.empty((1, H, 128, 128), dtype=torch.float32, device="cuda")
-    dims = kda.make_dims(q, v)
+    dims = kda.make_dims(q, v, g=g)
     ws = kda.workspace_for(dims, "cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -176,7 +183,7 @@ def main():
     path_gbs = counts["bytes"] / (ms_step * 1e-3) / 1e9
 
     kernels = {
-        "intra": (intra_ms, INTRA_BYTES_PER_TH * th, ["kda_intra_bf16.hip", "kda_device.h", "kda_chunks.h"]),
+        "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th, ["kda_intra_bf16.hip", "kda_device.h", "kda_chunks.h"]),
         "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * H,
                   ["kda_inter_bf16.hip", "kda_device.h", "kda_chunks.h"]),
     }
@@ -184,10 +191,11 @@ def main():
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     digest = source_digest(dom_src)
-    traffic = traffic_for(dom, digest, 1)
+    traffic = traffic_for(dom, digest, w.name)
 
     rec = {
-        "metric": "KDA prefill tokens/s + TFLOP/s (% roofline), H=64 T=8192 K=V=128 bf16",
+        "metric": "KDA prefill tokens/s + TFLOP/s (% roofline), H=64 T=8192 K=V=128 bf16"
+                  + (" (scalar gate)" if w.gate == "scalar" else ""),
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -199,8 +207,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "heads": H, "tokens": T, "head_k": 128, "head_v": 128,
-                   "num_seqs": 1, "initial_state": False, "chunk": 16},
+        "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128,
+                   "num_seqs": 1, "initial_state": False, "chunk": 16, "gate": w.gate},
         "tflops": tflops,
         "tflops_frac": tflops / BF16_PEAK_TFLOPS,
         "path_hbm": {"algorithmic_bytes": counts["bytes"], "achieved": path_gbs, "peak": HBM_PEAK_GBS,

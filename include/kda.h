@@ -34,6 +34,8 @@
  *    v        [T, H, V]      io dtype
  *    out      [T, H, V]      io dtype     (bf16 results are rounded to nearest even)
  *    g        [T, H, K]      fp32         natural-log per-channel decay, alpha = exp(g)
+ *             [T, H]         fp32         with gate_kind = KDA_GATE_SCALAR: one decay per
+ *                                         token and head, the same for every channel
  *    beta     [T, H]         fp32
  *    states   [N, H, K, V]   fp32         initial_state (read), final_state (written)
  *    cu_seqlens [N + 1]      int32        sequence boundaries; NULL means one sequence
@@ -53,6 +55,13 @@ extern "C" {
 #define KDA_IO_BF16 0
 #define KDA_IO_F32 1
 
+/* layout of g. KDA_GATE_SCALAR is the scalar-gated delta rule (Gated DeltaNet), the
+ * other chunked delta-rule kernel FlashKDA's benchmark is compared with
+ * (tech-noisy.com, section "MoE通信とアテンション:MoonEPとFlashKDA"); it is KDA with
+ * g_t broadcast over the K channels, computed by the same kernels. */
+#define KDA_GATE_CHANNEL 0 /* g [T, H, K] */
+#define KDA_GATE_SCALAR 1  /* g [T, H]    */
+
 /* status codes */
 #define KDA_OK 0
 #define KDA_ERR_ARG (-1)         /* NULL required pointer, bad sizes, or num_seqs != 1 with NULL cu_seqlens */
@@ -69,7 +78,7 @@ typedef struct kda_dims {
     int32_t head_v;       /* V */
     int32_t num_seqs;     /* N >= 1 */
     int32_t io_dtype;     /* KDA_IO_BF16 or KDA_IO_F32 */
-    int32_t reserved;     /* must be 0 */
+    int32_t gate_kind;    /* KDA_GATE_CHANNEL (0) or KDA_GATE_SCALAR */
 } kda_dims_t;
 
 /* Bytes of device workspace kda_chunk_prefill / kda_intra_chunk / kda_inter_chunk need

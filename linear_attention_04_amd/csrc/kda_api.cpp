@@ -52,7 +52,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUN
 int make_geometry(const kda_dims_t *d, Geometry *g) {
     if (d == nullptr || g == nullptr) return KDA_ERR_ARG;
     if (d->total_tokens < 0 || d->num_heads < 1 || d->head_k < 1 || d->head_v < 1 || d->num_seqs < 1 ||
-        d->reserved != 0)
+        (d->gate_kind != KDA_GATE_CHANNEL && d->gate_kind != KDA_GATE_SCALAR))
         return KDA_ERR_ARG;
     if (d->total_tokens > (int64_t)INT32_MAX || d->num_seqs > (1 << 24) || d->num_heads > (1 << 16))
         return KDA_ERR_ARG;
@@ -63,6 +63,7 @@ int make_geometry(const kda_dims_t *d, Geometry *g) {
     g->V = d->head_v;
     g->N = d->num_seqs;
     g->io = d->io_dtype;
+    g->scalar_gate = d->gate_kind == KDA_GATE_SCALAR;
     // sum_n ceil(len_n / 16) <= (T + 15 N) / 16
     g->max_chunks = (g->T + 15 * (int64_t)g->N) / kChunk;
     if (g->max_chunks > (int64_t)INT32_MAX / 2) return KDA_ERR_ARG;

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64) void kda_intra_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ chunk_seq, int64_t T, int H, int N, int64_t max_chunks,
-    float *__restrict__ records) {
+    float *__restrict__ records, int scalar_gate) {
     __shared__ float qs[16 * K], ks[16 * K], G[16 * K];
     __shared__ float A[256], P[256], TB[256], MM[256], bs[16];
     const int tid = threadIdx.x;
@@ -48,7 +48,9 @@ __global__ __launch_bounds__(64) void kda_intra_f32_kernel(
         const size_t off = ((size_t)(start + r) * H + h) * K + ch;
         qs[idx] = ok ? q[off] : 0.f;
         ks[idx] = ok ? k[off] : 0.f;
-        G[idx] = ok ? g[off] : 0.f;
+        // a scalar gate (g [T, H]) is the same decay for every channel
+        const size_t goff = scalar_gate ? (size_t)(start + r) * H + h : off;
+        G[idx] = ok ? g[goff] : 0.f;
     }
     if (tid < 16) bs[tid] = tid < len ? beta[(size_t)(start + tid) * H + h] : 0.f;
     __syncthreads();
@@ -185,7 +187,7 @@ hipError_t intra_f32(const float *q, const float *k, const float *g, const float
     hipLaunchKernelGGL(kda_intra_f32_kernel<K>, grid, dim3(64), 0, stream, q, k, g, beta, cu,
                        reinterpret_cast<const int32_t *>(base + geo.off_chunk_off),
                        reinterpret_cast<const int32_t *>(base + geo.off_chunk_seq), geo.T, geo.H, geo.N,
-                       geo.max_chunks, reinterpret_cast<float *>(base + geo.off_records));
+                       geo.max_chunks, reinterpret_cast<float *>(base + geo.off_records), (int)geo.scalar_gate);
     return hipGetLastError();
 }
 

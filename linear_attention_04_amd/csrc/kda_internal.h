@@ -33,6 +33,7 @@ constexpr size_t rec_bytes_f32(int K) { return 4u * (3u * 16u * (size_t)K + 2u *
 struct Geometry {
     int64_t T;
     int H, K, V, N, io;
+    bool scalar_gate;        // g is [T, H] (one decay per token and head) instead of [T, H, K]
     int64_t max_chunks;      // upper bound on chunks over all sequences
     size_t off_chunk_off;    // int32 [N + 1]
     size_t off_chunk_seq;    // int32 [max_chunks]

@@ -51,6 +51,10 @@ __device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
     dst[3] = __uint_as_float(raw.y & 0xffff0000u);
 }
 
+// SCALAR_GATE: g is [T, H], one decay per token and head for all channels (the
+// scalar-gated delta rule); the per-channel gate arithmetic below then works on
+// one value per lane, which the compiler shares across the channels.
+template <bool SCALAR_GATE>
 __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
@@ -81,13 +85,18 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     const int64_t t = start + c;
     float kr[32], qr[32], gr[32];
     const size_t rowoff = ((size_t)(row_ok ? t : start) * H + h) * KD + 4 * grp;
+    const float gs = (SCALAR_GATE && row_ok) ? g[(size_t)t * H + h] : 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (row_ok) {
             load_bf16x4(q + rowoff + 16 * j, qr + 4 * j);
             load_bf16x4(k + rowoff + 16 * j, kr + 4 * j);
-            const float4 gv = *reinterpret_cast<const float4 *>(g + rowoff + 16 * j);
-            gr[4 * j] = gv.x; gr[4 * j + 1] = gv.y; gr[4 * j + 2] = gv.z; gr[4 * j + 3] = gv.w;
+            if (SCALAR_GATE) {
+                gr[4 * j] = gr[4 * j + 1] = gr[4 * j + 2] = gr[4 * j + 3] = gs;
+            } else {
+                const float4 gv = *reinterpret_cast<const float4 *>(g + rowoff + 16 * j);
+                gr[4 * j] = gv.x; gr[4 * j + 1] = gv.y; gr[4 * j + 2] = gv.z; gr[4 * j + 3] = gv.w;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) { qr[4 * j + i] = 0.f; kr[4 * j + i] = 0.f; gr[4 * j + i] = 0.f; }
@@ -263,7 +272,8 @@ hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const
     const int64_t blocks = geo.max_chunks * ((geo.H + kWaves - 1) / kWaves);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
-    hipLaunchKernelGGL(kda_intra_bf16_kernel, grid, dim3(64 * kWaves), 0, stream,
+    auto kern = geo.scalar_gate ? kda_intra_bf16_kernel<true> : kda_intra_bf16_kernel<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), 0, stream,
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), g, beta,
                        cu_seqlens, chunk_off, chunk_seq, geo.T, geo.H, geo.N, geo.max_chunks,
                        base + geo.off_records);

@@ -15,7 +15,9 @@ mix, so every input here is synthetic:
 * v ~ N(0, 1).
 * beta = sigmoid(N(0, 1)), one scalar per token and head.
 * g = -s * softplus(N(0, 1)), one log-decay per token, head and key channel
-  (s = 0.1, or 0.02 for the long-context case).
+  (s = 0.1, or 0.02 for the long-context case); scalar-gate workloads (the
+  Gated DeltaNet comparison of that benchmark discussion) draw one per token and
+  head instead.
 * For bf16 workloads q, k and v are rounded to bf16 (round to nearest even);
   g, beta and the states stay fp32.
 * Initial states, where a workload has one, are 0.02 * N(0, 1) in fp32.
@@ -52,6 +54,7 @@ class Workload:
     has_initial_state: bool
     num_seqs: int = 1
     lengths: tuple | None = None  # explicit sequence lengths (else drawn, see seq_lengths)
+    gate: str = "channel"  # "channel": g [T, H, K]; "scalar": g [T, H]
 
     @property
     def bf16(self) -> bool:
@@ -73,14 +76,14 @@ WORKLOADS = {
 def custom_workload(name: str, seed: int, heads: int, total_tokens: int | None = None,
                     head_k: int = 128, head_v: int = 128, io_dtype: str = "bf16",
                     gate_scale: float = 0.1, has_initial_state: bool = False, num_seqs: int = 1,
-                    lengths=None) -> Workload:
+                    lengths=None, gate: str = "channel") -> Workload:
     """A workload with the standard value recipe at other sizes (parity tests).
     ``lengths`` fixes the packed sequence lengths (total_tokens and num_seqs follow)."""
     if lengths is not None:
         lengths = tuple(int(n) for n in lengths)
         total_tokens, num_seqs = sum(lengths), len(lengths)
     return Workload(name, seed, heads, total_tokens, head_k, head_v, io_dtype, gate_scale,
-                    has_initial_state, num_seqs, lengths)
+                    has_initial_state, num_seqs, lengths, gate)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -122,7 +125,7 @@ def generate_block(w: Workload, block: int) -> dict:
     k = rng.standard_normal((tb, H, K), dtype=np.float32)
     v = rng.standard_normal((tb, H, V), dtype=np.float32)
     beta = rng.standard_normal((tb, H), dtype=np.float32)
-    g = rng.standard_normal((tb, H, K), dtype=np.float32)
+    g = rng.standard_normal((tb, H) if w.gate == "scalar" else (tb, H, K), dtype=np.float32)
     q = _unit_rows(q) * np.float32(1.0 / np.sqrt(K))
     k = _unit_rows(k)
     beta = _sigmoid(beta)
@@ -170,7 +173,7 @@ def initial_state(w: Workload) -> np.ndarray | None:
 def generate(w: Workload, threads: int | None = None) -> dict:
     """All inputs of ``w`` as fp32 numpy arrays (bf16-exact values for bf16 workloads).
 
-    Keys: q, k, v [T,H,K|V]; g [T,H,K]; beta [T,H]; cu_seqlens int32[N+1];
+    Keys: q, k, v [T,H,K|V]; g [T,H,K] ([T,H] for a scalar gate); beta [T,H]; cu_seqlens int32[N+1];
     initial_state [N,H,K,V] or None.
     """
     nb = num_blocks(w)
@@ -179,7 +182,7 @@ def generate(w: Workload, threads: int | None = None) -> dict:
         "q": np.empty((T, H, K), np.float32),
         "k": np.empty((T, H, K), np.float32),
         "v": np.empty((T, H, V), np.float32),
-        "g": np.empty((T, H, K), np.float32),
+        "g": np.empty((T, H) if w.gate == "scalar" else (T, H, K), np.float32),
         "beta": np.empty((T, H), np.float32),
     }
 
@@ -209,13 +212,15 @@ def algorithmic_counts(w: Workload, chunk: int = 16) -> dict:
     Per token and head: 6KV flops for the three state contractions (W.S, Q+.S and
     the rank-16 state update) plus 2C(3K+2V) for the in-chunk products (A, P, W,
     U and P.Delta). Compulsory bytes: q, k, v, out in the io dtype, g and beta in
-    fp32, plus every initial and final state read or written (fp32).
+    fp32 (g is K values per token and head, or one for a scalar gate), plus every
+    initial and final state read or written (fp32).
     """
     K, V, C = w.head_k, w.head_v, chunk
     th = w.total_tokens * w.heads
     flops = th * (6 * K * V + 2 * C * (3 * K + 2 * V))
     es = 2 if w.bf16 else 4
-    bytes_tok = es * (2 * K + V) + 4 * K + 4 + es * V
+    gate_bytes = 4 if w.gate == "scalar" else 4 * K
+    bytes_tok = es * (2 * K + V) + gate_bytes + 4 + es * V
     states = w.num_seqs * w.heads * K * V * 4
     n_states = 1 + (1 if w.has_initial_state else 0)
     return {"flops": flops, "bytes": th * bytes_tok + n_states * states,

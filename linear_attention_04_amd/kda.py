@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_IO_BF16 = 0
 KDA_IO_F32 = 1
+KDA_GATE_CHANNEL = 0
+KDA_GATE_SCALAR = 1
 KDA_OK = 0
 KDA_ERR_ARG = -1
 KDA_ERR_UNSUPPORTED = -2
@@ -41,7 +43,7 @@ class KdaDims(ctypes.Structure):
         ("head_v", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32),
         ("io_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("gate_kind", ctypes.c_int32),
     ]
 
 
@@ -119,14 +121,16 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def make_dims(q, v, cu_seqlens=None) -> KdaDims:
+def make_dims(q, v, cu_seqlens=None, g=None) -> KdaDims:
+    """Sizes from the tensors; a g of shape [T, H] selects the scalar gate."""
     import torch
 
     T, H, K = q.shape
     V = v.shape[2]
     io = KDA_IO_BF16 if q.dtype == torch.bfloat16 else KDA_IO_F32
     N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
-    return KdaDims(T, H, K, V, N, io, 0)
+    gate = KDA_GATE_SCALAR if (g is not None and g.dim() == 2) else KDA_GATE_CHANNEL
+    return KdaDims(T, H, K, V, N, io, gate)
 
 
 def workspace_for(dims: KdaDims, device):
@@ -156,15 +160,17 @@ def _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
     T, H, K = q.shape
-    if k.shape != (T, H, K) or g.shape != (T, H, K) or v.shape[:2] != (T, H) or beta.shape != (T, H):
-        raise ValueError("shape mismatch: q, k, g [T,H,K], v [T,H,V], beta [T,H]")
+    if k.shape != (T, H, K) or g.shape not in ((T, H, K), (T, H)) or v.shape[:2] != (T, H) \
+            or beta.shape != (T, H):
+        raise ValueError("shape mismatch: q, k [T,H,K], g [T,H,K] or [T,H], v [T,H,V], beta [T,H]")
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None,
                   final_state=True, workspace=None, stream=None):
     """Chunked KDA prefill on the current device.
 
-    q, k: [T, H, K]; v: [T, H, V] (bf16 or fp32); g: [T, H, K] fp32; beta: [T, H] fp32;
+    q, k: [T, H, K]; v: [T, H, V] (bf16 or fp32); beta: [T, H] fp32;
+    g: [T, H, K] fp32 (per-channel gate) or [T, H] fp32 (scalar gate, Gated DeltaNet);
     cu_seqlens: int32 [N+1] or None; initial_state: [N, H, K, V] fp32 or None.
     final_state: True to allocate and return it, a tensor to write into, or None.
     Returns (out, final_state).
@@ -172,7 +178,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=Non
     import torch
 
     _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
-    dims = make_dims(q, v, cu_seqlens)
+    dims = make_dims(q, v, cu_seqlens, g)
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if final_state is True:

@@ -67,6 +67,9 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, heads=None,
 
     q, k, g: [T, H, K]; v: [T, H, V]; beta: [T, H] (any float dtype; converted to
     fp32, which must already hold the exact values the GPU sees).
+    g may also be [T, H]: the scalar-gated delta rule, which is this recurrence with
+    the one decay of a token and head applied to every key channel (the Gated
+    DeltaNet comparison in tech-noisy.com, "MoE通信とアテンション:MoonEPとFlashKDA").
     cu_seqlens: int [N+1] or None (one sequence). initial_state: [N, H, K, V] or None.
     heads: iterable of head indices to evaluate (default: all).
     Returns (out [T, n_heads, V] float64 or None, final_state [N, n_heads, K, V] float64 or None).
@@ -74,6 +77,8 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, heads=None,
     lib = _load(lib_path)
     q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
     T, H, K = q.shape
+    if g.shape == (T, H):
+        g = np.ascontiguousarray(np.broadcast_to(g[:, :, None], (T, H, K)))
     V = v.shape[2]
     if k.shape != (T, H, K) or g.shape != (T, H, K) or v.shape[:2] != (T, H) or beta.shape != (T, H):
         raise ValueError("inconsistent input shapes")

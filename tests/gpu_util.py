@@ -97,11 +97,12 @@ def generate_on_device(w, keep_heads, threads: int = 16):
     torch = torch_mod()
     T, H, K, V = w.total_tokens, w.heads, w.head_k, w.head_v
     io = torch.bfloat16 if w.bf16 else torch.float32
+    gshape = (T, H) if w.gate == "scalar" else (T, H, K)
     dev = {
         "q": torch.empty((T, H, K), dtype=io, device="cuda"),
         "k": torch.empty((T, H, K), dtype=io, device="cuda"),
         "v": torch.empty((T, H, V), dtype=io, device="cuda"),
-        "g": torch.empty((T, H, K), dtype=torch.float32, device="cuda"),
+        "g": torch.empty(gshape, dtype=torch.float32, device="cuda"),
         "beta": torch.empty((T, H), dtype=torch.float32, device="cuda"),
     }
     keep = list(keep_heads)
@@ -109,7 +110,7 @@ def generate_on_device(w, keep_heads, threads: int = 16):
         "q": np.empty((T, len(keep), K), np.float32),
         "k": np.empty((T, len(keep), K), np.float32),
         "v": np.empty((T, len(keep), V), np.float32),
-        "g": np.empty((T, len(keep), K), np.float32),
+        "g": np.empty((T, len(keep)) + gshape[2:], np.float32),
         "beta": np.empty((T, len(keep)), np.float32),
     }
 

@@ -22,8 +22,8 @@ def _need_gpu():
     kda.load_library()
 
 
-def _run(name, keep):
-    w = inputs.WORKLOADS[name]
+def _run(name, keep, w=None):
+    w = w or inputs.WORKLOADS[name]
     print(f"workload {name}: heads kept for the oracle {keep}", flush=True)
     dev, host = gu.generate_on_device(w, keep)
     out, fs = gu.run_gpu(dev)
@@ -44,3 +44,9 @@ def test_fullsize_all_heads(name):
 
 def test_fullsize_long_context_sampled_heads():
     _run("long_h64_t131072_s0", [0, 21, 42, 63])
+
+
+def test_fullsize_scalar_gate_all_heads():
+    """The scalar-gated delta rule at the benchmark shape (g [T, H])."""
+    w = inputs.custom_workload("fixed_h64_t8192_scalar_gate", 1, 64, 8192, gate="scalar")
+    _run(w.name, list(range(64)), w)

@@ -21,9 +21,9 @@ def _need_gpu():
     kda.load_library()  # fails loudly when the HIP library is missing
 
 
-def _case(name, seed, H, T=None, K=128, io="bf16", state=False, gate=0.1, lengths=None):
+def _case(name, seed, H, T=None, K=128, io="bf16", state=False, gate=0.1, lengths=None, gate_kind="channel"):
     w = inputs.custom_workload(name, seed, heads=H, total_tokens=T, head_k=K, head_v=K, io_dtype=io,
-                               gate_scale=gate, has_initial_state=state, lengths=lengths)
+                               gate_scale=gate, has_initial_state=state, lengths=lengths, gate=gate_kind)
     return w, inputs.generate(w)
 
 
@@ -240,3 +240,37 @@ def test_intra_chunk_intermediates_match_chunked_reference():
                 tol = 3e-4 if key in ("TB", "MM") else 6e-3
                 assert rel <= tol, (key, h, ci, rel, max_abs)
             assert np.max(np.abs(gam_full / it["gamma"] - 1)) <= 2e-6
+
+
+@pytest.mark.parametrize("T", [16, 333])
+def test_bf16_scalar_gate(T):
+    """g [T, H]: one decay per token and head (the scalar-gated delta rule)."""
+    w, x = _case(f"bf16_sg_t{T}", 80 + T, H=5, T=T, state=True, gate_kind="scalar")
+    _check(w, x, False)
+
+
+def test_bf16_scalar_gate_packed():
+    w, x = _case("bf16_sg_packed", 91, H=4, lengths=(40, 1, 0, 77, 16), state=True, gate_kind="scalar")
+    _check(w, x, True)
+
+
+@pytest.mark.parametrize("K", [16, 128])
+def test_f32_scalar_gate(K):
+    w, x = _case(f"f32_sg_k{K}", 95 + K, H=3, T=53, K=K, io="f32", state=True, gate_kind="scalar")
+    _check(w, x, False)
+
+
+def test_scalar_gate_equals_broadcast_channel_gate():
+    """The scalar-gate kernels must give what the per-channel kernels give for the
+    same gate repeated over the channels (both run on the GPU; bf16 io)."""
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    w, x = _case("bf16_sg_vs_cg", 99, H=3, T=200, state=True, gate_kind="scalar")
+    d = gu.upload(x, True, False)
+    out_s, fs_s = gu.run_gpu(d)
+    d["g"] = d["g"][:, :, None].expand(-1, -1, 128).contiguous()
+    out_c, fs_c = gu.run_gpu(d)
+    gu.assert_close("out", gu.to_host(out_s), gu.to_host(out_c).astype(np.float64), True)
+    gu.assert_close("final_state", gu.to_host(fs_s), gu.to_host(fs_c), True)
+    assert kda.KDA_GATE_SCALAR == 1

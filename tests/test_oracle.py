@@ -132,3 +132,39 @@ def test_oracle_matches_stored_golden():
     assert x["cu_seqlens"].tolist() == doc["cu_seqlens"]
     assert np.max(np.abs(o - np.array(doc["out"]))) <= 1e-14
     assert np.max(np.abs(fs - np.array(doc["final_state"]))) <= 1e-14
+
+
+def test_scalar_gate_is_the_scalar_decay_delta_rule():
+    """A [T, H] gate: the oracle must apply the token's one decay to every key channel,
+    i.e. S <- (I - beta k k^T) (alpha S) + beta k v^T with a scalar alpha = exp(g),
+    written out here with explicit K x K matrices for tiny sizes."""
+    rng = np.random.default_rng(7)
+    T, H, K, V = 9, 2, 4, 3
+    q = rng.standard_normal((T, H, K)).astype(np.float32)
+    k = rng.standard_normal((T, H, K)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, V)).astype(np.float32)
+    g = (-0.3 * rng.random((T, H))).astype(np.float32)
+    beta = rng.random((T, H)).astype(np.float32)
+    s0 = rng.standard_normal((1, H, K, V)).astype(np.float32)
+    out, fs = oracle.prefill(q, k, v, g, beta, initial_state=s0)
+    for h in range(H):
+        S = s0[0, h].astype(np.float64)
+        for t in range(T):
+            a = np.exp(np.float64(g[t, h]))
+            kt = k[t, h].astype(np.float64)
+            keep = np.eye(K) - np.float64(beta[t, h]) * np.outer(kt, kt)
+            S = keep @ (a * S) + np.float64(beta[t, h]) * np.outer(kt, v[t, h].astype(np.float64))
+            np.testing.assert_allclose(out[t, h], S.T @ q[t, h].astype(np.float64), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(fs[0, h], S, rtol=1e-12, atol=1e-13)
+
+
+def test_scalar_gate_generator_shapes():
+    w = inputs.custom_workload("sg", 5, 3, 40, head_k=16, head_v=16, io_dtype="f32", gate="scalar")
+    x = inputs.generate(w)
+    assert x["g"].shape == (40, 3) and np.all(x["g"] <= 0)
+    w2 = inputs.custom_workload("cg", 5, 3, 40, head_k=16, head_v=16, io_dtype="f32")
+    x2 = inputs.generate(w2)
+    # the gate is drawn last in each block, so the other tensors are unchanged
+    for name in ("q", "k", "v", "beta"):
+        np.testing.assert_array_equal(x[name], x2[name])
