@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--gate", choices=("channel", "scalar"), default="channel",
                     help="scalar: the same shape with one gate per token and head (Gated DeltaNet)")
+    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
+                    help="decode: one-token state update of --decode-batch sequences x 64 heads")
+    ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM counters)")
     return ap.parse_args()
@@ -108,6 +111,83 @@ def cpu_baseline(x, w, min_seconds: float = 10.0, max_repeats: int = 64):
     }
 
 
+def decode_bench(args):
+    """One decode step (kda_decode_step) of B sequences x 64 heads per timed step;
+    state [B, 64, 128, 128] fp32 read and written in place."""
+    import numpy as np
+    import torch
+
+    from linear_attention_04_amd import inputs, kda
+
+    B, H = args.decode_batch, 64
+    w = inputs.custom_workload(f"decode_b{B}_h{H}", 1, H, B, gate=args.gate)
+    x = inputs.generate(w)
+    rng = np.random.default_rng([1, 7])
+    s0 = (0.02 * rng.standard_normal((B, H, 128, 128))).astype(np.float32)
+    dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
+                         if bf else torch.from_numpy(a).to("cuda"))
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    g, beta = dev(x["g"], False), dev(x["beta"], False)
+    state = torch.from_numpy(s0).to("cuda")
+    out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    dims = kda.KdaDims(B, H, 128, 128, B, kda.KDA_IO_BF16,
+                       kda.KDA_GATE_SCALAR if args.gate == "scalar" else kda.KDA_GATE_CHANNEL)
+
+    def step():
+        st = kda.kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                 state.data_ptr(), out.data_ptr(), dims, stream.cuda_stream)
+        if st:
+            raise kda.KdaError(st, "decode")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_step = wall * 1e3 / args.steps
+    gate_bytes = 4 if args.gate == "scalar" else 512
+    per_bh = 2 * 128 * 128 * 4 + 4 * 256 + gate_bytes + 4  # state in + out, q k v out, g, beta
+    alg = per_bh * B * H
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "KDA decode step tokens/s (one token per sequence, state update in place)",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_k": 128, "head_v": 128, "gate": args.gate},
+        "kernels_ms": {"decode": kern_ms},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for("decode", source_digest(["kda_decode.hip", "kda_device.h"]), w.name),
+                     "algorithmic_bytes": alg, "source_digest": source_digest(["kda_decode.hip", "kda_device.h"])},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.max_threads()
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=np.arange(B + 1),
+                           initial_state=s0)
+            runs += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or runs >= 10000:
+                break
+        rec["cpu_baseline"] = {"value": runs * B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"the whole step ({B} sequences x {H} heads) run {runs} times, {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +207,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration()
     kda.load_library()
+    if args.mode == "decode":
+        return decode_bench(args)
     if args.gate == "scalar":
         w = inputs.custom_workload(SCALAR_GATE_WORKLOAD, 1, 64, 8192, gate="scalar")
     else:

@@ -112,6 +112,23 @@ int kda_inter_chunk(const void *v, const int32_t *cu_seqlens, const float *initi
                     void *out, float *final_state, const kda_dims_t *dims,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step (serving): a batch of B sequences, one new token each, updates
+ * every (sequence, head) state in place and writes that token's output. A deployment
+ * keeps each head's fixed-size state between calls and updates it per token instead
+ * of growing a cache (augursoft.site "Kimi K3 的三個系統設計", section
+ * "第一個設計：把長上下文從「一直累積」改成「持續更新狀態」"). Per (sequence, head):
+ *     S <- Diag(alpha) S,  delta = beta (v - S^T k),  S <- S + k delta^T,  o = S^T q.
+ * dims: total_tokens = num_seqs = B (B = 0 does nothing), num_heads = H,
+ *       head_k = head_v = 128, io_dtype KDA_IO_BF16 or KDA_IO_F32, gate_kind either.
+ * Layouts: q, k [B, H, K] and v, out [B, H, V] in the io dtype; g [B, H, K] or [B, H]
+ *          (scalar gate) and beta [B, H] fp32; state [B, H, K, V] fp32, read and
+ *          overwritten. The arithmetic is fp32; bf16 out is rounded to nearest even.
+ * No workspace. Returns KDA_ERR_ARG (bad sizes, NULL pointer), KDA_ERR_UNSUPPORTED
+ * (K or V not 128), KDA_ERR_ALIGN, KDA_ERR_LAUNCH, or KDA_OK. `state` must not alias
+ * any other argument. */
+int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    float *state, void *out, const kda_dims_t *dims, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);
 

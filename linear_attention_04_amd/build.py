@@ -22,6 +22,7 @@ SOURCES = [
     "kda_intra_bf16.hip",
     "kda_inter_bf16.hip",
     "kda_f32.hip",
+    "kda_decode.hip",
 ]
 
 ARCH = "gfx950"

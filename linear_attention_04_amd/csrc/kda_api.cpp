@@ -148,6 +148,25 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
                            stream);
 }
 
+int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    float *state, void *out, const kda_dims_t *dims, void *stream) {
+    if (dims == nullptr) return KDA_ERR_ARG;
+    if (dims->total_tokens < 0 || dims->num_heads < 1 || dims->num_seqs < 0 ||
+        dims->total_tokens != (int64_t)dims->num_seqs ||
+        (dims->gate_kind != KDA_GATE_CHANNEL && dims->gate_kind != KDA_GATE_SCALAR) ||
+        (dims->io_dtype != KDA_IO_BF16 && dims->io_dtype != KDA_IO_F32))
+        return KDA_ERR_ARG;
+    if (dims->total_tokens * (int64_t)dims->num_heads > (int64_t)INT32_MAX) return KDA_ERR_ARG;
+    if (dims->head_k != 128 || dims->head_v != 128) return KDA_ERR_UNSUPPORTED;
+    if (dims->total_tokens == 0) return KDA_OK;
+    const int st = kda::check_pointers({q, k, v, g, beta, state, out}, {});
+    if (st != KDA_OK) return st;
+    return kda::launch_status(kda::launch_decode(q, k, v, g, beta, state, out, dims->total_tokens,
+                                                 dims->num_heads, dims->io_dtype,
+                                                 dims->gate_kind == KDA_GATE_SCALAR,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 const char *kda_status_string(int status) {
     switch (status) {
     case KDA_OK: return "ok";
@@ -160,6 +179,6 @@ const char *kda_status_string(int status) {
     }
 }
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 200; }
 
 }  // extern "C"

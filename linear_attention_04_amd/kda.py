@@ -30,6 +30,7 @@ EXPORTS = (
     "kda_chunk_prefill",
     "kda_intra_chunk",
     "kda_inter_chunk",
+    "kda_decode_step",
     "kda_status_string",
     "kda_version",
 )
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_intra_chunk.restype = i32
     lib.kda_inter_chunk.argtypes = [p, p, p, p, p, dims_p, p, sz, p]
     lib.kda_inter_chunk.restype = i32
+    lib.kda_decode_step.argtypes = [p, p, p, p, p, p, p, dims_p, p]
+    lib.kda_decode_step.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -103,6 +106,10 @@ def kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state, dims: KdaDim
                     workspace_bytes: int, stream) -> int:
     return int(load_library().kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state,
                                               ctypes.byref(dims), workspace, workspace_bytes, stream))
+
+
+def kda_decode_step(q, k, v, g, beta, state, out, dims: KdaDims, stream) -> int:
+    return int(load_library().kda_decode_step(q, k, v, g, beta, state, out, ctypes.byref(dims), stream))
 
 
 def kda_status_string(status: int) -> str:
@@ -193,3 +200,34 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=Non
     if st != KDA_OK:
         raise KdaError(st, "kda_chunk_prefill")
     return out, final_state
+
+
+def decode_step(q, k, v, g, beta, state, out=None, stream=None):
+    """One decode step for B sequences: q, k [B, H, K], v [B, H, V] (bf16 or fp32),
+    g [B, H, K] or [B, H] fp32, beta [B, H] fp32, state [B, H, K, V] fp32 (updated in
+    place). Returns out [B, H, V]."""
+    import torch
+
+    io = q.dtype
+    B, H, K = q.shape
+    V = v.shape[2]
+    for name, t, dt in (("k", k, io), ("v", v, io), ("g", g, torch.float32), ("beta", beta, torch.float32),
+                        ("state", state, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if k.shape != (B, H, K) or v.shape[:2] != (B, H) or g.shape not in ((B, H, K), (B, H)) \
+            or beta.shape != (B, H) or state.shape != (B, H, K, V):
+        raise ValueError("shape mismatch: q, k [B,H,K], v [B,H,V], g [B,H,K] or [B,H], beta [B,H], "
+                         "state [B,H,K,V]")
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    dims = KdaDims(B, H, K, V, B, KDA_IO_BF16 if io == torch.bfloat16 else KDA_IO_F32,
+                   KDA_GATE_SCALAR if g.dim() == 2 else KDA_GATE_CHANNEL)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    st = kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out), dims, s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_step")
+    return out

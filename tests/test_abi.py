@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: libkda.so loads, exports every function include/kda.h
+declares, and its host-side logic (sizes, argument checks, status strings) behaves
+as documented. Every call here returns before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_04_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from linear_attention_04_amd import build
+
+        build.build()
+    return kda.load_library()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert kda.kda_version() >= 200
+    for st in (kda.KDA_OK, kda.KDA_ERR_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_ALIGN,
+               kda.KDA_ERR_WORKSPACE, kda.KDA_ERR_LAUNCH):
+        s = kda.kda_status_string(st)
+        assert isinstance(s, str) and s
+    assert kda.kda_status_string(12345)
+
+
+def dims(T=64, H=2, K=128, V=128, N=1, io=kda.KDA_IO_BF16, gate=kda.KDA_GATE_CHANNEL):
+    return kda.KdaDims(T, H, K, V, N, io, gate)
+
+
+def test_workspace_bytes(lib):
+    a = kda.kda_workspace_bytes(dims(T=64))
+    b = kda.kda_workspace_bytes(dims(T=6400))
+    assert 0 < a < b
+    # chunk records grow linearly with the chunk count (16 tokens) and the heads
+    assert kda.kda_workspace_bytes(dims(T=6400, H=4)) > b
+    assert kda.kda_workspace_bytes(dims(gate=kda.KDA_GATE_SCALAR)) == a
+    assert kda.kda_workspace_bytes(dims(io=kda.KDA_IO_F32, K=16, V=16)) > 0
+    # invalid or unsupported sizes give 0
+    assert kda.kda_workspace_bytes(dims(K=64, V=64)) == 0          # bf16 needs K = V = 128
+    assert kda.kda_workspace_bytes(dims(io=kda.KDA_IO_F32, K=16, V=32)) == 0
+    assert kda.kda_workspace_bytes(dims(H=0)) == 0
+    assert kda.kda_workspace_bytes(dims(T=-1)) == 0
+    assert kda.kda_workspace_bytes(dims(gate=7)) == 0
+    assert kda.kda_workspace_bytes(dims(io=9)) == 0
+
+
+class Buf:
+    """Host memory standing in for device pointers: the calls below fail their
+    checks before anything dereferences them."""
+
+    def __init__(self, n=1 << 16):
+        self.raw = ctypes.create_string_buffer(n + 64)
+        base = ctypes.addressof(self.raw)
+        self.ptr = (base + 63) // 64 * 64
+
+    def at(self, off=0):
+        return self.ptr + off
+
+
+def test_prefill_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    d = dims()
+    ws_need = kda.kda_workspace_bytes(d)
+    # missing required pointer
+    assert kda.kda_chunk_prefill(None, p, p, p, p, None, None, p, None, d, p, ws_need, None) == kda.KDA_ERR_ARG
+    # misaligned pointer
+    assert kda.kda_chunk_prefill(b.at(4), p, p, p, p, None, None, p, None, d, p, ws_need, None) == kda.KDA_ERR_ALIGN
+    # workspace too small or missing
+    assert kda.kda_chunk_prefill(p, p, p, p, p, None, None, p, None, d, p, ws_need - 1, None) == \
+        kda.KDA_ERR_WORKSPACE
+    assert kda.kda_chunk_prefill(p, p, p, p, p, None, None, p, None, d, None, ws_need, None) == \
+        kda.KDA_ERR_WORKSPACE
+    # several sequences need cu_seqlens
+    d2 = dims(N=2)
+    assert kda.kda_chunk_prefill(p, p, p, p, p, None, None, p, None, d2, p, 1 << 40, None) == kda.KDA_ERR_ARG
+    # unsupported head size
+    assert kda.kda_chunk_prefill(p, p, p, p, p, None, None, p, None, dims(K=64, V=64), p, 1 << 40, None) == \
+        kda.KDA_ERR_UNSUPPORTED
+    # the two halves check the same way
+    assert kda.kda_intra_chunk(None, p, p, p, None, d, p, ws_need, None) == kda.KDA_ERR_ARG
+    assert kda.kda_inter_chunk(p, None, None, None, None, d, p, ws_need, None) == kda.KDA_ERR_ARG
+    assert kda.kda_inter_chunk(p, None, b.at(8), p, None, d, p, ws_need, None) == kda.KDA_ERR_ALIGN
+
+
+def test_decode_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    ok = dims(T=4, N=4)
+    # B = 0 is a no-op that succeeds without touching anything
+    assert kda.kda_decode_step(None, None, None, None, None, None, None, dims(T=0, N=0), None) == kda.KDA_OK
+    assert kda.kda_decode_step(None, p, p, p, p, p, p, ok, None) == kda.KDA_ERR_ARG
+    assert kda.kda_decode_step(p, p, p, p, p, b.at(4), p, ok, None) == kda.KDA_ERR_ALIGN
+    # one token per sequence
+    assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=2), None) == kda.KDA_ERR_ARG
+    assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=4, K=64, V=64), None) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=4, gate=3), None) == kda.KDA_ERR_ARG

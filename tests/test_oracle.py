@@ -168,3 +168,26 @@ def test_scalar_gate_generator_shapes():
     # the gate is drawn last in each block, so the other tensors are unchanged
     for name in ("q", "k", "v", "beta"):
         np.testing.assert_array_equal(x[name], x2[name])
+
+
+def test_one_token_sequences_are_single_decode_steps():
+    """A batch of one-token sequences from given states (the decode step's reading):
+    each state takes exactly one step S <- (I - b k k^T) Diag(exp g) S + b k v^T and the
+    output is S^T q, written out with explicit matrices."""
+    rng = np.random.default_rng(17)
+    B, H, K, V = 5, 2, 6, 4
+    q = rng.standard_normal((B, H, K)).astype(np.float32)
+    k = rng.standard_normal((B, H, K)).astype(np.float32)
+    v = rng.standard_normal((B, H, V)).astype(np.float32)
+    g = (-0.5 * rng.random((B, H, K))).astype(np.float32)
+    beta = rng.random((B, H)).astype(np.float32)
+    s0 = rng.standard_normal((B, H, K, V)).astype(np.float32)
+    out, fs = oracle.prefill(q, k, v, g, beta, cu_seqlens=np.arange(B + 1), initial_state=s0)
+    f = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    for b in range(B):
+        for h in range(H):
+            kk = f(k[b, h])
+            S = (np.eye(K) - f(beta[b, h]) * np.outer(kk, kk)) @ np.diag(np.exp(f(g[b, h]))) @ f(s0[b, h]) \
+                + f(beta[b, h]) * np.outer(kk, f(v[b, h]))
+            np.testing.assert_allclose(fs[b, h], S, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(out[b, h], S.T @ f(q[b, h]), rtol=1e-12, atol=1e-12)
