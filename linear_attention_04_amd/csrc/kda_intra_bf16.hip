@@ -33,15 +33,29 @@ constexpr int KD = 128;
 constexpr int kWaves = 4;
 constexpr int kChStride = 20;  // LDS elements per channel in channel-major tiles (16 tokens + 4 pad)
 
+// One wave's LDS. K^d, A and K+ have disjoint lifetimes and share one area:
+// K^d (A/P products -> its record store), A (forward substitution), K+ (W and
+// M K+ products). At 12.9 KiB per wave, three 4-wave workgroups fit in a CU.
 struct alignas(16) IntraLds {
-    float kp[KD * kChStride];   // K+ channel-major [channel][token]
-    __bf16 kd[KD * kChStride];  // K^d channel-major, bf16
-    float a[256];               // A row-major [r][i]
-    float p[256];               // P row-major
-    float tb[256];              // T' row-major
-    float gam[KD];              // gamma = exp(G_C) per channel
+    union {
+        float kp[KD * kChStride];   // K+ channel-major [channel][token]
+        __bf16 kd[KD * kChStride];  // K^d channel-major, bf16
+        float a[256];               // A row-major [r][i]
+    };
+    float p[256];   // P row-major
+    float tb[256];  // T' row-major
+    float gam[KD];  // gamma = exp(G_C) per channel
     float beta[16];
 };
+
+// Every wave works in its own LDS area, so ordering among the lanes of one wave is
+// all that is needed: LDS accesses of a wave execute in program order, and this
+// keeps the compiler from moving them across the point.
+__device__ __forceinline__ void wave_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
     const uint2 raw = *reinterpret_cast<const uint2 *>(p);
@@ -144,8 +158,19 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
         acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
     }
 
+    wave_sync();
+    // K^d to the record now, so that its LDS area is free for A and K+
+    char *rec = records + ((size_t)h * max_chunks + chunk) * kRecBytesBf16;  // head-major
+    if (head_ok) {
+#pragma unroll
+        for (int mp = 0; mp < 4; ++mp) {
+            const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + c) * kChStride + 4 * grp]);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + 16 + c) * kChStride + 4 * grp]);
+            *reinterpret_cast<uint4 *>(rec + kRecKD + (mp * 64 + lane) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    }
     if (grp == 0) L.beta[c] = b;
-    __syncthreads();
+    wave_sync();
     const f32x4 brow = *reinterpret_cast<const f32x4 *>(&L.beta[4 * grp]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -153,7 +178,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
         L.a[r * 16 + c] = (c < r) ? brow[i] * acc_a[i] : 0.f;
         L.p[r * 16 + c] = (c <= r) ? acc_p[i] : 0.f;
     }
-    __syncthreads();
+    wave_sync();
 
     // ---- T = (I + A)^-1 by forward substitution; every lane solves column c ----
     float x[16];
@@ -183,7 +208,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
         if (c == 0) L.gam[ch] = gam;
     }
     const float *qp = qr;
-    __syncthreads();
+    wave_sync();
 
     // ---- M = P T' (row c, columns 4grp..4grp+3) ----
     const f32x4 tbrow = *reinterpret_cast<const f32x4 *>(&L.tb[c * 16 + 4 * grp]);
@@ -233,17 +258,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     }
 
     if (!head_ok) return;
-    char *rec = records + ((size_t)h * max_chunks + chunk) * kRecBytesBf16;  // head-major
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         *reinterpret_cast<bf16x8 *>(rec + kRecW + (s * 64 + lane) * 16) = wv[s];
         *reinterpret_cast<bf16x8 *>(rec + kRecQT + (s * 64 + lane) * 16) = qv[s];
-    }
-#pragma unroll
-    for (int mp = 0; mp < 4; ++mp) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + c) * kChStride + 4 * grp]);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + 16 + c) * kChStride + 4 * grp]);
-        *reinterpret_cast<uint4 *>(rec + kRecKD + (mp * 64 + lane) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
     bf16x8 tbv, mmv;
 #pragma unroll
