@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
                     help="decode: one-token state update of --decode-batch sequences x 64 heads")
     ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--fused", action="store_true",
+                    help="time the single-kernel form (kda_chunk_prefill_fused) instead of the split")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM counters)")
     return ap.parse_args()
@@ -227,6 +229,18 @@ def main():
     sp = stream.cuda_stream
 
     def step(e0=None, e1=None, e2=None):
+        if args.fused:
+            if e0 is not None:
+                e0.record(stream)
+            st = kda.kda_chunk_prefill_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                             None, None, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
+                                             ws.numel(), sp)
+            if e1 is not None:
+                e1.record(stream)
+                e2.record(stream)
+            if st:
+                raise kda.KdaError(st, "fused prefill")
+            return
         if e0 is not None:
             e0.record(stream)
         st = kda.kda_intra_chunk(q.data_ptr(), k.data_ptr(), g.data_ptr(), beta.data_ptr(), None, dims,
@@ -269,6 +283,10 @@ def main():
         "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * H,
                   ["kda_inter_bf16.hip", "kda_device.h", "kda_chunks.h"]),
     }
+    if args.fused:
+        # one launch; its algorithmic bytes are the path's compulsory bytes
+        kernels = {"fused": (intra_ms, counts["bytes"], ["kda_inter_bf16.hip", "kda_intra_wave.h", "kda_device.h",
+                                                         "kda_chunks.h"])}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -277,7 +295,7 @@ def main():
 
     rec = {
         "metric": "KDA prefill tokens/s + TFLOP/s (% roofline), H=64 T=8192 K=V=128 bf16"
-                  + (" (scalar gate)" if w.gate == "scalar" else ""),
+                  + (" (scalar gate)" if w.gate == "scalar" else "") + (" (single-kernel ablation)" if args.fused else ""),
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -290,12 +308,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128,
-                   "num_seqs": 1, "initial_state": False, "chunk": 16, "gate": w.gate},
+                   "num_seqs": 1, "initial_state": False, "chunk": 16, "gate": w.gate,
+                   "kernels": "fused" if args.fused else "split"},
         "tflops": tflops,
         "tflops_frac": tflops / BF16_PEAK_TFLOPS,
         "path_hbm": {"algorithmic_bytes": counts["bytes"], "achieved": path_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": path_gbs / HBM_PEAK_GBS},
-        "kernels_ms": {"intra": intra_ms, "inter": inter_ms},
+        "kernels_ms": {"fused": intra_ms} if args.fused else {"intra": intra_ms, "inter": inter_ms},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": dom_bytes, "source_digest": digest},

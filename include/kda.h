@@ -112,6 +112,21 @@ int kda_inter_chunk(const void *v, const int32_t *cu_seqlens, const float *initi
                     void *out, float *final_state, const kda_dims_t *dims,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Single-kernel form of kda_chunk_prefill, kept for the ablation that compares it
+ * with the two-kernel split (augursoft.site "Kimi K3 的三個系統設計", section
+ * "為什麼 FlashKDA 選擇 16-token chunks": FlashKDA's split into a token-parallel and a
+ * recurrent kernel beat one fused kernel). One launch; each recurrent workgroup
+ * builds the intra-chunk factors of its own head in LDS, so nothing but inputs,
+ * outputs and states goes through device memory. Same arguments, layouts, workspace
+ * and results as kda_chunk_prefill (bitwise: the same arithmetic in the same order);
+ * bf16 io only (KDA_ERR_UNSUPPORTED otherwise). The workspace holds only the chunk
+ * table here. */
+int kda_chunk_prefill_fused(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const int32_t *cu_seqlens,
+                            const float *initial_state, void *out, float *final_state,
+                            const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* One decode step (serving): a batch of B sequences, one new token each, updates
  * every (sequence, head) state in place and writes that token's output. A deployment
  * keeps each head's fixed-size state between calls and updates it per token instead

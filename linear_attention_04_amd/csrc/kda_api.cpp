@@ -148,6 +148,28 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
                            stream);
 }
 
+int kda_chunk_prefill_fused(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const int32_t *cu_seqlens, const float *initial_state, void *out, float *final_state,
+                            const kda_dims_t *dims, void *workspace, size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = kda::check_common(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st != KDA_OK) return st;
+    if (geo.io != KDA_IO_BF16) return KDA_ERR_UNSUPPORTED;
+    if (geo.T > 0) {
+        st = kda::check_pointers({q, k, v, g, beta, out}, {initial_state, final_state});
+    } else {
+        st = kda::check_pointers({}, {q, k, v, g, beta, out, initial_state, final_state});
+    }
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cu_seqlens != nullptr) {
+        st = kda::launch_status(kda::launch_chunk_table(cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    return kda::launch_status(kda::launch_fused_bf16(q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                                     final_state, geo, workspace, s));
+}
+
 int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                     float *state, void *out, const kda_dims_t *dims, void *stream) {
     if (dims == nullptr) return KDA_ERR_ARG;

@@ -32,6 +32,7 @@
 #include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_intra_wave.h"
 
 namespace kda {
 namespace {
@@ -323,6 +324,48 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     if (j < nchunks) step(j, opa, opb);
 }
 
+// The compute waves' part of a recurrent workgroup: the state slice in, the chunk
+// loop over the LDS ring, the state slice out. Compute wave (vt, kh) owns value
+// columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63.
+template <int DEPTH>
+__device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
+                                             size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
+                                             const float *__restrict__ s0, unsigned short *__restrict__ out,
+                                             float *__restrict__ sT) {
+    const int c = lane & 15, grp = lane >> 4;
+    const int vt = wid >> 1, kh = wid & 1;
+    lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
+    f32x4 S[4];
+    const size_t sbase = (size_t)pair * KD * VD + (size_t)(64 * kh) * VD + col0 + vt * 16 + c;
+    if (s0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Settle the state loads here: otherwise the counter wait that guards S's first
+    // use sits inside the chunk loop and, since stores count on the same counter,
+    // makes every chunk wait for the previous chunk's output store to complete.
+    wait_vmcnt<0>();
+    char *o0 = reinterpret_cast<char *>(out) + tok_bytes;
+    const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
+    const int64_t tok_rows = sc.tok_end - sc.tok_begin;
+    if (kh == 0)
+        compute_wave<0, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
+    else
+        compute_wave<1, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
+
+    if (sT) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
+    }
+}
+
 template <int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
@@ -338,7 +381,6 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
-    const int c = lane & 15, grp = lane >> 4;
     const int col0 = vg * kNW * 16;  // first value column of the workgroup
     const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
@@ -380,37 +422,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
         return;
     }
 
-    // ---- compute wave (vt, kh): value columns col0 + 16 vt .. + 15, rows 64 kh .. + 63 ----
-    const int vt = wid >> 1, kh = wid & 1;
-    lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
-    f32x4 S[4];
-    const size_t sbase = (size_t)pair * KD * VD + (size_t)(64 * kh) * VD + col0 + vt * 16 + c;
-    if (s0) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
-    } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // Settle the state loads here: otherwise the counter wait that guards S's first
-    // use sits inside the chunk loop and, since stores count on the same counter,
-    // makes every chunk wait for the previous chunk's output store to complete.
-    wait_vmcnt<0>();
-    char *o0 = reinterpret_cast<char *>(out) + tok_bytes;
-    const int64_t tok_rows = sc.tok_end - sc.tok_begin;
-    if (kh == 0)
-        compute_wave<0, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
-    else
-        compute_wave<1, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
-
-    if (sT) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
-    }
+    compute_role<DEPTH>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
 }
 
 template <int DEPTH>
@@ -431,6 +443,83 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Single-kernel ablation: the same recurrent workgroup, with the intra-chunk work
+// done inside it. The pages report that FlashKDA's split into a token-parallel
+// and a recurrent kernel beat one fused kernel, in which the token-parallel work
+// ran at the recurrence's low parallelism (augursoft.site "Kimi K3 的三個系統設計",
+// section "為什麼 FlashKDA 選擇 16-token chunks"). Here the two producer waves are
+// replaced by kIntraWaves waves that build each chunk's record (intra::chunk_record,
+// the intra-chunk kernel's own per-wave code) straight into the LDS ring and load
+// its value tile; nothing goes through HBM but q, k, v, g, beta, out and the states.
+// Each column group of a head builds the head's records itself.
+//
+// Intra wave i builds chunks i, i + kIntraWaves, ...: chunk m right after passing
+// B_{m - kIntraWaves} (chunks below kIntraWaves before B_0). Its slot last held chunk
+// m - kFusedDepth, which the compute waves finished reading before they reached
+// B_{m - kFusedDepth + 1} = B_{m - kIntraWaves}; they read chunk m after B_m. An
+// intra wave busy with a chunk holds every barrier until it is done, so the intra
+// waves work in step, kIntraWaves chunks at a time, alternating with the chain.
+constexpr int kIntraWaves = 4;
+constexpr int kFusedDepth = kIntraWaves + 1;
+constexpr int kFusedWaves = kComputeWaves + kIntraWaves;
+constexpr size_t kFusedLds = (size_t)kFusedDepth * kSlotBytes + kXchgBytes + kIntraWaves * sizeof(intra::IntraLds);
+static_assert(kFusedLds <= 160 * 1024, "LDS of one CU");
+
+template <bool SCALAR_GATE>
+__global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const unsigned short *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
+    float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks) {
+    extern __shared__ __attribute__((aligned(1024))) char ring[];  // slots, exchange, intra scratch
+    int pair, vg;
+    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    if (pair >= N * H) return;  // whole workgroup
+    const int n = pair / H, h = pair % H;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int col0 = vg * kNW * 16;
+    const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
+    const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
+
+    LaneOffsets lo;
+    lo.vrow = (unsigned int)H * VD * 2;
+    const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
+    const size_t chunk_rows = (size_t)16 * lo.vrow;
+
+    if (wid >= kComputeWaves) {
+        // ---- intra wave ----
+        const int i = wid - kComputeWaves;
+        intra::IntraLds &L = *reinterpret_cast<intra::IntraLds *>(
+            ring + kFusedDepth * kSlotBytes + kXchgBytes + i * sizeof(intra::IntraLds));
+        const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
+        auto produce = [&](int64_t m) {
+            const int64_t start = sc.tok_begin + 16 * m;
+            const int64_t rem = sc.tok_end - start;
+            const int len = rem >= 16 ? 16 : (int)rem;
+            char *slot = ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(m % kFusedDepth) * kSlotBytes);
+            intra::chunk_record<SCALAR_GATE>(q, k, g, beta, start, len, h, H, true, L, slot, lane);
+            // value tile [16 tokens][32 columns] bf16, lane: token lane / 4, 8 columns;
+            // rows past the end of the chunk are zero
+            const int row = lane >> 2;
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (row < len)
+                val = *reinterpret_cast<const uint4 *>(v0 + (size_t)m * chunk_rows + (size_t)row * lo.vrow +
+                                                       (lane & 3) * 16);
+            *reinterpret_cast<uint4 *>(slot + kVOff + lane * 16) = val;
+            wait_lgkm0();  // the slot is complete in LDS before this wave's next barrier
+        };
+        if (i < nchunks) produce(i);
+        for (int64_t b = 0; b <= nchunks; ++b) {
+            barrier();  // B_b
+            if (b % kIntraWaves == i && b + kIntraWaves < nchunks) produce(b + kIntraWaves);
+        }
+        return;
+    }
+    compute_role<kFusedDepth>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
+}
+
 }  // namespace
 
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
@@ -443,6 +532,27 @@ hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const flo
     const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
     if (blocks <= kCUs) return launch<8>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
     return launch<4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+}
+
+}  // namespace kda
+
+namespace kda {
+
+hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
+                             const Geometry &geo, const void *ws, hipStream_t stream) {
+    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
+    const char *base = static_cast<const char *>(ws);
+    const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
+    auto kern = geo.scalar_gate ? kda_fused_bf16_kernel<true> : kda_fused_bf16_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kFusedWaves), kFusedLds, stream,
+                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+                       static_cast<const unsigned short *>(v), g, beta, cu_seqlens, chunk_off, s0,
+                       static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks);
+    return hipGetLastError();
 }
 
 }  // namespace kda

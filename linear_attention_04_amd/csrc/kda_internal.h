@@ -52,6 +52,9 @@ hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const
                              hipStream_t stream);
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream);
+hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
+                             const Geometry &geo, const void *ws, hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          float *state, void *out, int64_t B, int H, int io, bool scalar_gate, hipStream_t stream);
 hipError_t launch_intra_f32(const float *q, const float *k, const float *g, const float *beta,

@@ -1,0 +1,263 @@
+// kda_intra_wave.h -- one wave's intra-chunk work for one (16-token chunk, head),
+// bf16 io, K = V = 128: from q, k, g, beta to the chunk's record (W, Q~, K^d, T',
+// M, gamma) in the layout the recurrent kernels read. Used by the intra-chunk
+// kernel (records to HBM) and by the fused prefill (records into the recurrent
+// workgroup's LDS ring).
+//
+// Per chunk, with S0 the state at the chunk start and G_r = g_1 + ... + g_r the
+// running log-gate, the recurrence becomes (I + A) Delta = diag(beta)(V - K+ S0) with
+//   A[r,i] = beta_r sum_c k[r,c] k[i,c] exp(G[r,c] - G[i,c])  (i < r),
+//   P[r,i] =        sum_c q[r,c] k[i,c] exp(G[r,c] - G[i,c])  (i <= r),
+// K+ = k * exp(G), Q+ = q * exp(G), K^d = k * exp(G_C - G), gamma = exp(G_C).
+// With T = (I + A)^-1 and T' = T diag(beta): Delta = T' V - W S0 with W = T' K+,
+// and the chunk output O = Q+ S0 + P Delta = Q~ S0 + M V with M = P T' and
+// Q~ = Q+ - M K+ (augursoft.site "Kimi K3 的三個系統設計", section
+// "為什麼 FlashKDA 選擇 16-token chunks": 16-token chunks and a 16 x 16 inversion).
+//
+// Numerics: gates enter A and P through exp(G - G_ref) and exp(G_ref - G) with
+// G_ref the running gate at the chunk's 8th token, so both factors stay in range
+// for any gate the chunk can hold in fp32 (|G_C| < ~80). A and P, W and M K+ use
+// two-term bf16 splits (x = x_hi + x_lo) of their factors for ~16-bit accuracy;
+// W, Q~ and K^d are rounded to bf16 once, at the end.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace intra {
+
+constexpr int KD = 128;
+constexpr int kChStride = 20;  // LDS elements per channel in channel-major tiles (16 tokens + 4 pad)
+
+// One wave's LDS. K^d, A and K+ have disjoint lifetimes and share one area:
+// K^d (A/P products -> its record store), A (forward substitution), K+ (W and
+// M K+ products). At 12.9 KiB per wave, three 4-wave workgroups fit in a CU.
+struct alignas(16) IntraLds {
+    union {
+        float kp[KD * kChStride];   // K+ channel-major [channel][token]
+        __bf16 kd[KD * kChStride];  // K^d channel-major, bf16
+        float a[256];               // A row-major [r][i]
+    };
+    float p[256];   // P row-major
+    float tb[256];  // T' row-major
+    float gam[KD];  // gamma = exp(G_C) per channel
+    float beta[16];
+};
+
+// Every wave works in its own LDS area, so ordering among the lanes of one wave is
+// all that is needed: LDS accesses of a wave execute in program order, and this
+// keeps the compiler from moving them across the point.
+__device__ __forceinline__ void wave_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
+    const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+    dst[0] = __uint_as_float(raw.x << 16);
+    dst[1] = __uint_as_float(raw.x & 0xffff0000u);
+    dst[2] = __uint_as_float(raw.y << 16);
+    dst[3] = __uint_as_float(raw.y & 0xffff0000u);
+}
+
+// The record of chunk [start, start + len) of head h (len in 1..16), written to
+// `rec` (global or LDS memory) unless !head_ok (then the wave only computes, as a
+// stand-in that keeps its workgroup's waves in step). SCALAR_GATE: g is [T, H],
+// one decay per token and head for all channels (the scalar-gated delta rule); the
+// per-channel gate arithmetic then works on one value per lane, which the
+// compiler shares across the channels. Lane l holds token l % 16 of the chunk.
+template <bool SCALAR_GATE>
+__device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+                                             const float *__restrict__ g, const float *__restrict__ beta,
+                                             int64_t start, int len, int h, int H, bool head_ok, IntraLds &L,
+                                             char *rec, int lane) {
+    const int c = lane & 15;
+    const int grp = lane >> 4;
+
+    // ---- load: lane holds token c, channels 16j + 4grp + i (element e = 4j + i) ----
+    const bool row_ok = c < len;
+    const int64_t t = start + c;
+    float kr[32], qr[32], gr[32];
+    const size_t rowoff = ((size_t)(row_ok ? t : start) * H + h) * KD + 4 * grp;
+    const float gs = (SCALAR_GATE && row_ok) ? g[(size_t)t * H + h] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (row_ok) {
+            load_bf16x4(q + rowoff + 16 * j, qr + 4 * j);
+            load_bf16x4(k + rowoff + 16 * j, kr + 4 * j);
+            if (SCALAR_GATE) {
+                gr[4 * j] = gr[4 * j + 1] = gr[4 * j + 2] = gr[4 * j + 3] = gs;
+            } else {
+                const float4 gv = *reinterpret_cast<const float4 *>(g + rowoff + 16 * j);
+                gr[4 * j] = gv.x; gr[4 * j + 1] = gv.y; gr[4 * j + 2] = gv.z; gr[4 * j + 3] = gv.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { qr[4 * j + i] = 0.f; kr[4 * j + i] = 0.f; gr[4 * j + i] = 0.f; }
+        }
+    }
+    const float b = row_ok ? beta[(size_t)t * H + h] : 0.f;
+
+    // ---- running log-gate over the chunk's tokens (16-lane DPP scan), in place ----
+#pragma unroll
+    for (int e = 0; e < 32; ++e) gr[e] = row_inclusive_sum(gr[e]);
+    float *G = gr;
+
+    // ---- A and P on the MFMA: two-term bf16 splits of both factors. Gate factors
+    // up = exp(G - G_ref), dn = exp(G_ref - G) with G_ref the running gate at token 7;
+    // K^d = k exp(G_C - G) = k dn exp(G_C - G_ref) goes to LDS right away. ----
+    f32x4 acc_a = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = 8 * s + 2 * u;
+            const float d0 = G[e] - row_bcast<7>(G[e]), d1 = G[e + 1] - row_bcast<7>(G[e + 1]);
+            const float up0 = __expf(d0), up1 = __expf(d1);
+            const float dn0 = __expf(-d0), dn1 = __expf(-d1);
+            const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);  // channel of e; e + 1 is ch + 1
+            L.kd[ch * kChStride + c] = to_bf16(kr[e] * (dn0 * row_bcast<15>(up0)));
+            L.kd[(ch + 1) * kChStride + c] = to_bf16(kr[e + 1] * (dn1 * row_bcast<15>(up1)));
+            split_pair(kr[e] * up0, kr[e + 1] * up1, khh[u], khl[u]);
+            split_pair(qr[e] * up0, qr[e + 1] * up1, qhh[u], qhl[u]);
+            split_pair(kr[e] * dn0, kr[e + 1] * dn1, kbh[u], kbl[u]);
+        }
+        const bf16x8 vkhh = __builtin_bit_cast(bf16x8, make_uint4(khh[0], khh[1], khh[2], khh[3]));
+        const bf16x8 vkhl = __builtin_bit_cast(bf16x8, make_uint4(khl[0], khl[1], khl[2], khl[3]));
+        const bf16x8 vkbh = __builtin_bit_cast(bf16x8, make_uint4(kbh[0], kbh[1], kbh[2], kbh[3]));
+        const bf16x8 vkbl = __builtin_bit_cast(bf16x8, make_uint4(kbl[0], kbl[1], kbl[2], kbl[3]));
+        const bf16x8 vqhh = __builtin_bit_cast(bf16x8, make_uint4(qhh[0], qhh[1], qhh[2], qhh[3]));
+        const bf16x8 vqhl = __builtin_bit_cast(bf16x8, make_uint4(qhl[0], qhl[1], qhl[2], qhl[3]));
+        acc_a = mfma_16x16x32(vkhh, vkbh, acc_a);
+        acc_a = mfma_16x16x32(vkhl, vkbh, acc_a);
+        acc_a = mfma_16x16x32(vkhh, vkbl, acc_a);
+        acc_p = mfma_16x16x32(vqhh, vkbh, acc_p);
+        acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
+        acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
+    }
+
+    wave_sync();
+    // K^d to the record now, so that its LDS area is free for A and K+
+    if (head_ok) {
+#pragma unroll
+        for (int mp = 0; mp < 4; ++mp) {
+            const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + c) * kChStride + 4 * grp]);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + 16 + c) * kChStride + 4 * grp]);
+            *reinterpret_cast<uint4 *>(rec + kRecKD + (mp * 64 + lane) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    }
+    if (grp == 0) L.beta[c] = b;
+    wave_sync();
+    const f32x4 brow = *reinterpret_cast<const f32x4 *>(&L.beta[4 * grp]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        L.a[r * 16 + c] = (c < r) ? brow[i] * acc_a[i] : 0.f;
+        L.p[r * 16 + c] = (c <= r) ? acc_p[i] : 0.f;
+    }
+    wave_sync();
+
+    // ---- T = (I + A)^-1 by forward substitution; every lane solves column c ----
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc -= L.a[r * 16 + i] * x[i];
+        x[r] = acc;
+    }
+    // T'[r][c] = T[r][c] * beta_c (this lane's own token is c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float xi = grp == 0 ? x[i] : (grp == 1 ? x[4 + i] : (grp == 2 ? x[8 + i] : x[12 + i]));
+        L.tb[(4 * grp + i) * 16 + c] = xi * b;
+    }
+
+    // ---- K+ channel-major in LDS for the transposed operand; Q+ in place; gamma =
+    // exp(G_C) is token 15's exp(G), broadcast ----
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);
+        const float ep = __expf(G[e]);
+        L.kp[ch * kChStride + c] = kr[e] * ep;
+        qr[e] *= ep;
+        const float gam = row_bcast<15>(ep);
+        if (c == 0) L.gam[ch] = gam;
+    }
+    const float *qp = qr;
+    wave_sync();
+
+    // ---- M = P T' (row c, columns 4grp..4grp+3) ----
+    const f32x4 tbrow = *reinterpret_cast<const f32x4 *>(&L.tb[c * 16 + 4 * grp]);
+    f32x4 mrow = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        const float pck = L.p[c * 16 + kk];
+        const f32x4 trow = *reinterpret_cast<const f32x4 *>(&L.tb[kk * 16 + 4 * grp]);
+        mrow += pck * trow;
+    }
+    bf16x4 tbh, tbl, mmh, mml;
+    split_bf16x4(tbrow, tbh, tbl);
+    split_bf16x4(mrow, mmh, mml);
+    // B operands [X; X] over the 32-long reduction, for X = T'_hi, T'_lo, M_hi, M_lo
+    bf16x8 tbh2, tbl2, mmh2, mml2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tbh2[i] = tbh2[4 + i] = tbh[i];
+        tbl2[i] = tbl2[4 + i] = tbl[i];
+        mmh2[i] = mmh2[4 + i] = mmh[i];
+        mml2[i] = mml2[4 + i] = mml[i];
+    }
+
+    // ---- W^T = K+^T T'^T and (M K+)^T = K+^T M^T, tile by tile of 16 channels.
+    // A operand [K+_hi | K+_lo]: ([K+_hi | K+_lo] . [X; X]) = (K+_hi + K+_lo) X. ----
+    bf16x8 wv[4], qv[4];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+        const f32x4 kpt = *reinterpret_cast<const f32x4 *>(&L.kp[(16 * jt + c) * kChStride + 4 * grp]);
+        bf16x4 kph, kpl;
+        split_bf16x4(kpt, kph, kpl);
+        bf16x8 kp2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { kp2[i] = kph[i]; kp2[4 + i] = kpl[i]; }
+        f32x4 wt = {0.f, 0.f, 0.f, 0.f};
+        wt = mfma_16x16x32(kp2, tbh2, wt);
+        wt = mfma_16x16x32(kp2, tbl2, wt);
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+        pt = mfma_16x16x32(kp2, mmh2, pt);
+        pt = mfma_16x16x32(kp2, mml2, pt);
+        // element e = 4 jt + i: slab jt >> 1, position 4 (jt & 1) + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wv[jt >> 1][4 * (jt & 1) + i] = to_bf16(wt[i]);
+            qv[jt >> 1][4 * (jt & 1) + i] = to_bf16(qp[4 * jt + i] - pt[i]);
+        }
+    }
+
+    if (!head_ok) return;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        *reinterpret_cast<bf16x8 *>(rec + kRecW + (s * 64 + lane) * 16) = wv[s];
+        *reinterpret_cast<bf16x8 *>(rec + kRecQT + (s * 64 + lane) * 16) = qv[s];
+    }
+    bf16x8 tbv, mmv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tbv[i] = tbh[i]; tbv[4 + i] = tbl[i];
+        mmv[i] = mmh[i]; mmv[4 + i] = mml[i];
+    }
+    *reinterpret_cast<bf16x8 *>(rec + kRecTB + lane * 16) = tbv;
+    *reinterpret_cast<bf16x8 *>(rec + kRecMM + lane * 16) = mmv;
+    if (c < 8) {
+        // gamma_perm[grp][4c + i] = gamma[16c + 4grp + i]
+        const float4 gv = *reinterpret_cast<const float4 *>(&L.gam[16 * c + 4 * grp]);
+        *reinterpret_cast<float4 *>(rec + kRecGAM + (grp * 32 + 4 * c) * 4) = gv;
+    }
+}
+
+}  // namespace intra
+}  // namespace kda

@@ -28,6 +28,7 @@ KDA_ERR_LAUNCH = -5
 EXPORTS = (
     "kda_workspace_bytes",
     "kda_chunk_prefill",
+    "kda_chunk_prefill_fused",
     "kda_intra_chunk",
     "kda_inter_chunk",
     "kda_decode_step",
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_workspace_bytes.restype = sz
     lib.kda_chunk_prefill.argtypes = [p, p, p, p, p, p, p, p, p, dims_p, p, sz, p]
     lib.kda_chunk_prefill.restype = i32
+    lib.kda_chunk_prefill_fused.argtypes = [p, p, p, p, p, p, p, p, p, dims_p, p, sz, p]
+    lib.kda_chunk_prefill_fused.restype = i32
     lib.kda_intra_chunk.argtypes = [p, p, p, p, p, dims_p, p, sz, p]
     lib.kda_intra_chunk.restype = i32
     lib.kda_inter_chunk.argtypes = [p, p, p, p, p, dims_p, p, sz, p]
@@ -94,6 +97,13 @@ def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_st
     return int(load_library().kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out,
                                                 final_state, ctypes.byref(dims), workspace,
                                                 workspace_bytes, stream))
+
+
+def kda_chunk_prefill_fused(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, dims: KdaDims,
+                            workspace, workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_chunk_prefill_fused(q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                                      final_state, ctypes.byref(dims), workspace,
+                                                      workspace_bytes, stream))
 
 
 def kda_intra_chunk(q, k, g, beta, cu_seqlens, dims: KdaDims, workspace, workspace_bytes: int,
@@ -173,13 +183,14 @@ def _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state):
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None,
-                  final_state=True, workspace=None, stream=None):
+                  final_state=True, workspace=None, stream=None, fused=False):
     """Chunked KDA prefill on the current device.
 
     q, k: [T, H, K]; v: [T, H, V] (bf16 or fp32); beta: [T, H] fp32;
     g: [T, H, K] fp32 (per-channel gate) or [T, H] fp32 (scalar gate, Gated DeltaNet);
     cu_seqlens: int32 [N+1] or None; initial_state: [N, H, K, V] fp32 or None.
     final_state: True to allocate and return it, a tensor to write into, or None.
+    fused: run the single-kernel form (kda_chunk_prefill_fused; bf16 only).
     Returns (out, final_state).
     """
     import torch
@@ -194,11 +205,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=Non
     if workspace is None:
         workspace = workspace_for(dims, q.device)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    st = kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                           _ptr(initial_state), _ptr(out), _ptr(final_state), dims, _ptr(workspace),
-                           workspace.numel(), s)
+    entry = kda_chunk_prefill_fused if fused else kda_chunk_prefill
+    st = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(initial_state),
+               _ptr(out), _ptr(final_state), dims, _ptr(workspace), workspace.numel(), s)
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_prefill")
+        raise KdaError(st, entry.__name__)
     return out, final_state
 
 

@@ -50,3 +50,17 @@ def test_fullsize_scalar_gate_all_heads():
     """The scalar-gated delta rule at the benchmark shape (g [T, H])."""
     w = inputs.custom_workload("fixed_h64_t8192_scalar_gate", 1, 64, 8192, gate="scalar")
     _run(w.name, list(range(64)), w)
+
+
+def test_fused_fullsize_equals_split():
+    """The single-kernel ablation at the benchmark shape, bitwise against the split."""
+    import torch
+
+    from linear_attention_04_amd import kda
+
+    w = inputs.WORKLOADS["fixed_h64_t8192"]
+    dev, _ = gu.generate_on_device(w, [])
+    out_s, fs_s = gu.run_gpu(dev)
+    out_f, fs_f = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_f) and torch.equal(fs_s, fs_f)

@@ -274,3 +274,47 @@ def test_scalar_gate_equals_broadcast_channel_gate():
     gu.assert_close("out", gu.to_host(out_s), gu.to_host(out_c).astype(np.float64), True)
     gu.assert_close("final_state", gu.to_host(fs_s), gu.to_host(fs_c), True)
     assert kda.KDA_GATE_SCALAR == 1
+
+
+def _fused_vs_split(w, x, packed):
+    """The single-kernel ablation runs the same per-wave arithmetic as the two-kernel
+    path, so its results must be bitwise equal; the split path is itself checked
+    against the oracle."""
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    print(f"case fused {w.name}: H={w.heads} T={w.total_tokens} N={w.num_seqs} gate={w.gate}", flush=True)
+    d = gu.upload(x, True, packed)
+    out_s, fs_s = gu.run_gpu(d)
+    out_f, fs_f = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                                    initial_state=d["initial_state"], fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_f), "fused out differs from the two-kernel path"
+    assert torch.equal(fs_s, fs_f), "fused final state differs from the two-kernel path"
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 333])
+def test_fused_equals_split_bitwise(T):
+    w, x = _case(f"fused_t{T}", 120 + T, H=5, T=T, state=True)
+    _fused_vs_split(w, x, False)
+
+
+def test_fused_packed_ragged_and_scalar_gate():
+    w, x = _case("fused_packed", 131, H=4, state=True, lengths=[1, 15, 16, 17, 47, 0, 64, 100, 3])
+    _fused_vs_split(w, x, True)
+    w, x = _case("fused_sg", 132, H=3, T=200, state=True, gate_kind="scalar")
+    _fused_vs_split(w, x, False)
+
+
+def test_fused_matches_oracle():
+    w, x = _case("fused_oracle", 133, H=6, T=300, state=True)
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    d = gu.upload(x, True, False)
+    out, fs = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"],
+                                fused=True)
+    torch.cuda.synchronize()
+    ro, rs = gu.run_oracle(x, False)
+    gu.assert_close("out", gu.to_host(out), ro, True)
+    gu.assert_close("final_state", gu.to_host(fs), rs, True)
