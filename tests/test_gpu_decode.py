@@ -128,3 +128,28 @@ def test_decode_empty_batch():
 
     d = kda.KdaDims(0, 4, 128, 128, 0, kda.KDA_IO_BF16, kda.KDA_GATE_CHANNEL)
     assert kda.kda_decode_step(None, None, None, None, None, None, None, d, None) == kda.KDA_OK
+
+
+def test_decode_graph_replay():
+    """The decode step captured in a HIP graph: each replay advances the state in place
+    and equals an eager step from the same state."""
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    B, H = 5, 4
+    w, x = _batch(41, B, H)
+    d = gu.upload(x, True, False)
+    st = torch.from_numpy(x["state"]).to("cuda")
+    out = torch.empty_like(d["v"])
+    kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st.clone(), out=out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, out=out)
+    for rep in range(3):
+        ref_state = st.clone()
+        ref_out = kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], ref_state)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(st, ref_state), f"replay {rep} differs"

@@ -318,3 +318,52 @@ def test_fused_matches_oracle():
     ro, rs = gu.run_oracle(x, False)
     gu.assert_close("out", gu.to_host(out), ro, True)
     gu.assert_close("final_state", gu.to_host(fs), rs, True)
+
+
+@pytest.mark.parametrize("H", [1, 3, 7])
+def test_bf16_head_counts_not_multiple_of_four(H):
+    """Head counts that leave idle waves in the intra-chunk workgroups and idle
+    workgroups in the recurrent grid (rounded up to 8 (sequence, head) pairs)."""
+    w, x = _case(f"bf16_h{H}", 140 + H, H=H, T=70, state=True)
+    _check(w, x, False)
+
+
+def test_bf16_many_short_sequences():
+    """150 packed sequences of 0..40 tokens (many empty or shorter than a chunk)."""
+    rng = np.random.default_rng(150)
+    lengths = [int(n) for n in rng.integers(0, 41, size=150)]
+    lengths[0], lengths[-1] = 0, 0
+    w, x = _case("bf16_many", 151, H=3, state=True, lengths=lengths)
+    _check(w, x, True)
+
+
+def test_prefill_graph_replay():
+    """kda_chunk_prefill captured once in a HIP graph and replayed with new inputs,
+    eager work and synchronisation between replays; every replay equals the eager call."""
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    w, x = _case("graph_a", 160, H=4, T=200, state=True)
+    d = gu.upload(x, True, False)
+    dims = kda.make_dims(d["q"], d["v"])
+    ws = kda.workspace_for(dims, "cuda")
+    out = torch.empty_like(d["v"])
+    fs = torch.empty_like(d["initial_state"])
+    kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"], out=out,
+                      final_state=fs, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"], out=out,
+                          final_state=fs, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _, xr = _case(f"graph_r{rep}", 161 + rep, H=4, T=200, state=True)
+        dr = gu.upload(xr, True, False)
+        for name in ("q", "k", "v", "g", "beta", "initial_state"):
+            d[name].copy_(dr[name])
+        ref_out, ref_fs = gu.run_gpu(dr)  # eager, on fresh buffers
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(fs, ref_fs), f"replay {rep} differs from the eager call"
