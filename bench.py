@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="prefill workload (default: the H=64, T=8192 benchmark shape); see inputs.WORKLOADS")
     ap.add_argument("--gate", choices=("channel", "scalar"), default="channel",
                     help="scalar: the same shape with one gate per token and head (Gated DeltaNet)")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
@@ -99,7 +101,9 @@ def cpu_baseline(x, w, min_seconds: float = 10.0, max_repeats: int = 64):
     threads = oracle.max_threads()
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], want_out=True, want_state=True)
+        oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                       cu_seqlens=x["cu_seqlens"] if w.num_seqs > 1 else None,
+                       initial_state=x["initial_state"], want_out=True, want_state=True)
         runs += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or runs >= max_repeats:
@@ -214,16 +218,24 @@ def main():
     if args.gate == "scalar":
         w = inputs.custom_workload(SCALAR_GATE_WORKLOAD, 1, 64, 8192, gate="scalar")
     else:
-        w = inputs.WORKLOADS[WORKLOAD]
+        w = inputs.WORKLOADS[args.workload]
+    if not w.bf16:
+        print("bench.py times the bf16 path; the fp32 workload is a parity case", file=sys.stderr)
+        return 2
     x = inputs.generate(w)
     dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
                          if bf else torch.from_numpy(a).to("cuda"))
     q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
     g, beta = dev(x["g"], False), dev(x["beta"], False)
-    T, H = w.total_tokens, w.heads
+    T, H, N = w.total_tokens, w.heads, w.num_seqs
+    cu = torch.from_numpy(x["cu_seqlens"]).to("cuda") if N > 1 else None
+    s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).to("cuda")
+    cu_p = None if cu is None else cu.data_ptr()
+    s0_p = None if s0 is None else s0.data_ptr()
+    n_states = 1 + (s0 is not None)
     out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
-    fs = torch.empty((1, H, 128, 128), dtype=torch.float32, device="cuda")
-    dims = kda.make_dims(q, v, g=g)
+    fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    dims = kda.make_dims(q, v, cu, g=g)
     ws = kda.workspace_for(dims, "cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -233,7 +245,7 @@ def main():
             if e0 is not None:
                 e0.record(stream)
             st = kda.kda_chunk_prefill_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
-                                             None, None, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
+                                             cu_p, s0_p, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
                                              ws.numel(), sp)
             if e1 is not None:
                 e1.record(stream)
@@ -243,11 +255,11 @@ def main():
             return
         if e0 is not None:
             e0.record(stream)
-        st = kda.kda_intra_chunk(q.data_ptr(), k.data_ptr(), g.data_ptr(), beta.data_ptr(), None, dims,
+        st = kda.kda_intra_chunk(q.data_ptr(), k.data_ptr(), g.data_ptr(), beta.data_ptr(), cu_p, dims,
                                  ws.data_ptr(), ws.numel(), sp)
         if e1 is not None:
             e1.record(stream)
-        st2 = kda.kda_inter_chunk(v.data_ptr(), None, None, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
+        st2 = kda.kda_inter_chunk(v.data_ptr(), cu_p, s0_p, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
                                   ws.numel(), sp)
         if e2 is not None:
             e2.record(stream)
@@ -279,8 +291,9 @@ def main():
     path_gbs = counts["bytes"] / (ms_step * 1e-3) / 1e9
 
     kernels = {
-        "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th, ["kda_intra_bf16.hip", "kda_device.h", "kda_chunks.h"]),
-        "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * H,
+        "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th,
+                  ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_device.h", "kda_chunks.h"]),
+        "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * w.num_seqs * H * n_states,
                   ["kda_inter_bf16.hip", "kda_device.h", "kda_chunks.h"]),
     }
     if args.fused:
@@ -294,8 +307,8 @@ def main():
     traffic = traffic_for(dom, digest, w.name)
 
     rec = {
-        "metric": "KDA prefill tokens/s + TFLOP/s (% roofline), H=64 T=8192 K=V=128 bf16"
-                  + (" (scalar gate)" if w.gate == "scalar" else "") + (" (single-kernel ablation)" if args.fused else ""),
+        "metric": (f"KDA prefill tokens/s + TFLOP/s (% roofline), H={H} T={T} K=V=128 bf16"
+                   + (" (scalar gate)" if w.gate == "scalar" else "") + (" (single-kernel ablation)" if args.fused else "")),
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -308,7 +321,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128,
-                   "num_seqs": 1, "initial_state": False, "chunk": 16, "gate": w.gate,
+                   "num_seqs": N, "initial_state": s0 is not None, "chunk": 16, "gate": w.gate,
                    "kernels": "fused" if args.fused else "split"},
         "tflops": tflops,
         "tflops_frac": tflops / BF16_PEAK_TFLOPS,
