@@ -197,9 +197,8 @@ def decode_bench(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads and sequences would shard without communication; see DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads and packed "
+              "sequences would shard across GPUs without communication).", file=sys.stderr)
         return 2
 
     import numpy as np
