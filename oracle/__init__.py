@@ -6,8 +6,10 @@ binding never do, and the two share no code.
 
 * ``kda_oracle.c`` / :func:`prefill` -- the plain token-by-token recurrence in
   double precision (the definition of the result).
+* ``kda_oracle.c`` / :func:`backward` -- its reverse-mode gradients, token by
+  token in double precision.
 * :mod:`oracle.reference` -- NumPy forms used to pin the oracle: the explicit
   K x K matrix product form, and the 16-token chunked form with its
   per-chunk intermediates.
 """
-from .kda_oracle import build, prefill, library_path, max_threads  # noqa: F401
+from .kda_oracle import backward, build, prefill, library_path, max_threads  # noqa: F401

@@ -97,3 +97,81 @@ def chunked(q, k, v, g, beta, S0=None, chunk=16, ref=None, intermediates=False):
     if intermediates:
         return o, S, inter
     return o, S
+
+
+def chunked_backward(q, k, v, g, beta, dO, S0=None, dST=None, chunk=16, ref=None):
+    """Gradients of L = <dO, o> + <dS_T, S_T> through the chunked form above.
+
+    One sequence of one head (shapes as :func:`chunked`, dO [T, V], dST [K, V]).
+    Returns dict(dq, dk, dv, dg, dbeta, dS0). The reverse pass runs over chunks;
+    R is the gradient reaching the chunk's end state. With the chunk's start
+    state S0 and U = V - K+ S0, Delta = T diag(beta) U:
+        dDelta = P^T dO + K^d R,      dU = (T diag(beta))^T dDelta,    dv = dU,
+        dQ+ = dO S0^T,  dK+ = -dU S0^T,  dK^d = Delta R^T,  dgamma = rowsum(R * S0),
+        dP = tril(dO Delta^T),  d(T diag(beta)) = dDelta U^T,
+        R <- Diag(gamma) R + Q+^T dO - K+^T dU   (the gradient reaching S0).
+    The triangular inverse gives dA = -T^T dT T^T (strictly lower part), and A,
+    P, K+, Q+, K^d, gamma pass their gradients to q, k, beta and the running
+    gate G, whose reverse running sum inside the chunk is dg. The reference
+    token factored out of A and P (as in :func:`chunked`) cancels in every
+    product, so no gradient flows through it.
+    """
+    q, k, v, g, beta, dO = map(_f64, (q, k, v, g, beta, dO))
+    T, K = k.shape
+    V = v.shape[1]
+    S = np.zeros((K, V)) if S0 is None else _f64(S0).copy()
+    starts = []
+    for c0 in range(0, T, chunk):
+        starts.append(S.copy())
+        _, S = chunked(q[c0:c0 + chunk], k[c0:c0 + chunk], v[c0:c0 + chunk], g[c0:c0 + chunk],
+                       beta[c0:c0 + chunk], S, chunk=chunk, ref=ref)
+    R = np.zeros((K, V)) if dST is None else _f64(dST).copy()
+    dq, dk, dg = np.zeros((T, K)), np.zeros((T, K)), np.zeros((T, K))
+    dv, dbeta = np.zeros((T, V)), np.zeros(T)
+    for ci in range(len(starts) - 1, -1, -1):
+        c0 = ci * chunk
+        c1 = min(c0 + chunk, T)
+        n = c1 - c0
+        qc, kc, vc, gc, bc, D = q[c0:c1], k[c0:c1], v[c0:c1], g[c0:c1], beta[c0:c1], dO[c0:c1]
+        S0c = starts[ci]
+        G = np.cumsum(gc, axis=0)
+        r = (n // 2) if ref is None else min(ref, n - 1)
+        up, dn = np.exp(G - G[r]), np.exp(G[r] - G)
+        k_hat, q_hat, k_rev = kc * up, qc * up, kc * dn
+        KK = k_hat @ k_rev.T
+        A = np.tril(bc[:, None] * KK, -1)
+        P = np.tril(q_hat @ k_rev.T, 0)
+        Tinv = np.linalg.inv(np.eye(n) + A)
+        Tb = Tinv * bc[None, :]
+        Kp, Qp = kc * np.exp(G), qc * np.exp(G)
+        Kd = kc * np.exp(G[-1] - G)
+        gamma = np.exp(G[-1])
+        U = vc - Kp @ S0c
+        Delta = Tb @ U
+
+        dDelta = P.T @ D + Kd @ R
+        dU = Tb.T @ dDelta
+        dv[c0:c1] = dU
+        dQp = D @ S0c.T
+        dKp = -dU @ S0c.T
+        dKd = Delta @ R.T
+        dgamma = np.sum(R * S0c, axis=1)
+        dP = np.tril(D @ Delta.T, 0)
+        dTb = dDelta @ U.T
+        dbeta_c = np.sum(dTb * Tinv, axis=0)
+        dT = dTb * bc[None, :]
+        dA = np.tril(-Tinv.T @ dT @ Tinv.T, -1)
+        dbeta_c += np.sum(dA * KK, axis=1)
+        dAt = dA * bc[:, None]
+        dk_hat = dAt @ k_rev
+        dk_rev = dAt.T @ k_hat + dP.T @ q_hat
+        dq_hat = dP @ k_rev
+
+        dkc = dk_hat * up + dk_rev * dn + dKp * np.exp(G) + dKd * np.exp(G[-1] - G)
+        dqc = dq_hat * up + dQp * np.exp(G)
+        dG = dk_hat * k_hat - dk_rev * k_rev + dq_hat * q_hat + dKp * Kp + dQp * Qp - dKd * Kd
+        dG[-1] += np.sum(dKd * Kd, axis=0) + dgamma * gamma
+        dg[c0:c1] = np.cumsum(dG[::-1], axis=0)[::-1]
+        dq[c0:c1], dk[c0:c1], dbeta[c0:c1] = dqc, dkc, dbeta_c
+        R = gamma[:, None] * R + Qp.T @ D - Kp.T @ dU
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dS0=R)

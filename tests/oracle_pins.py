@@ -176,3 +176,153 @@ ALL_CHECKS = [
     check_linear_in_values_and_state,
     check_value_column_independence,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Backward: each check takes a function with the signature of oracle.backward.
+
+_GRADS = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
+
+
+def _bwd_case(rng, T, H, K, V, N=1, scalar_gate=False):
+    q = rng.standard_normal((T, H, K)).astype(np.float32)
+    k = (rng.standard_normal((T, H, K)) / math.sqrt(K)).astype(np.float32)
+    v = rng.standard_normal((T, H, V)).astype(np.float32)
+    gshape = (T, H) if scalar_gate else (T, H, K)
+    g = (-0.4 * rng.random(gshape)).astype(np.float32)
+    beta = rng.random((T, H)).astype(np.float32)
+    s0 = (rng.standard_normal((N, H, K, V)) * 0.5).astype(np.float32)
+    do = rng.standard_normal((T, H, V)).astype(np.float32)
+    dsT = rng.standard_normal((N, H, K, V)).astype(np.float32)
+    return q, k, v, g, beta, s0, do, dsT
+
+
+def _fd_loss(q, k, v, g, beta, s0, do, dsT, cu):
+    """L = sum <dO, o> + <dS_T, S_T> from the explicit K x K transition products (fp64)."""
+    T, H, K = q.shape
+    if g.ndim == 2:
+        g = np.broadcast_to(g[:, :, None], (T, H, K))
+    total = 0.0
+    for n in range(len(cu) - 1):
+        a, b = cu[n], cu[n + 1]
+        for h in range(H):
+            o, S = reference.explicit_matrices(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h],
+                                               beta[a:b, h], s0[n, h])
+            total += np.sum(o * do[a:b, h]) + np.sum(S * dsT[n, h])
+    return total
+
+
+def _check_fd(run_bwd, case, cu, tol=1e-7):
+    q, k, v, g, beta, s0, do, dsT = case
+    got = run_bwd(q, k, v, g, beta, do, cu_seqlens=cu, initial_state=s0, d_final_state=dsT)
+    args = [x.astype(np.float64) for x in (q, k, v, g, beta, s0)]
+    eps = 1e-6
+    for ai, name in enumerate(_GRADS):
+        fd = np.zeros_like(args[ai])
+        for idx in np.ndindex(args[ai].shape):
+            up = [x.copy() for x in args]
+            dn = [x.copy() for x in args]
+            up[ai][idx] += eps
+            dn[ai][idx] -= eps
+            fd[idx] = (_fd_loss(*up, do, dsT, cu) - _fd_loss(*dn, do, dsT, cu)) / (2 * eps)
+        err = np.max(np.abs(fd - got[name]))
+        assert err <= tol * max(1.0, np.max(np.abs(fd))), (name, err)
+
+
+def check_bwd_finite_differences(run_bwd, seed=20):
+    """Every gradient equals central finite differences (fp64, step 1e-6) of the
+    loss computed from the explicit transition products: two packed sequences of
+    two heads, with initial states and a final-state gradient."""
+    rng = np.random.default_rng(seed)
+    _check_fd(run_bwd, _bwd_case(rng, 9, 2, 3, 2, N=2), np.array([0, 4, 9]))
+
+
+def check_bwd_finite_differences_scalar_gate(run_bwd, seed=21):
+    """As above for a [T, H] gate (one decay per token and head)."""
+    rng = np.random.default_rng(seed)
+    _check_fd(run_bwd, _bwd_case(rng, 7, 1, 3, 2, scalar_gate=True), np.array([0, 7]))
+
+
+def check_bwd_finite_differences_long(run_bwd, seed=22):
+    """A 70-token sequence (the state is recomputed block by block in the reverse
+    pass): finite differences again, on K = V = 2."""
+    rng = np.random.default_rng(seed)
+    case = list(_bwd_case(rng, 70, 1, 2, 2))
+    case[3] = (-0.05 * rng.random((70, 1, 2))).astype(np.float32)  # keep the state alive
+    _check_fd(run_bwd, tuple(case), np.array([0, 70]), tol=1e-6)
+
+
+def check_bwd_no_write_closed_form(run_bwd, seed=23):
+    """beta = 0: S_t = Diag(exp(G_t)) S0 with G_t = g_1 + ... + g_t, so with
+    R_t = sum_{s >= t} Diag(exp(G_s - G_t)) q_s dO_s^T + Diag(exp(G_T - G_t)) dS_T
+    (the gradient reaching S_t): dq_t = S_t dO_t, dk = dv = 0,
+    dbeta_t = (R_t^T k_t) . (v_t - S_t^T k_t),
+    dS0 = sum_s Diag(exp(G_s)) q_s dO_s^T + Diag(exp(G_T)) dS_T, and
+    dg_t[c] = sum_{s >= t} exp(G_s[c]) q_s[c] (S0 dO_s)[c] + exp(G_T[c]) sum_j S0[c,j] dS_T[c,j]."""
+    rng = np.random.default_rng(seed)
+    T, K, V = 12, 4, 3
+    q, k, v, g, _, s0, do, dsT = _bwd_case(rng, T, 1, K, V)
+    beta = np.zeros((T, 1), np.float32)
+    got = run_bwd(q, k, v, g, beta, do, initial_state=s0, d_final_state=dsT)
+    q64, k64, v64, g64, do64 = (x[:, 0].astype(np.float64) for x in (q, k, v, g, do))
+    S0, dST = s0[0, 0].astype(np.float64), dsT[0, 0].astype(np.float64)
+    G = np.cumsum(g64, axis=0)
+    for t in range(T):
+        St = np.exp(G[t])[:, None] * S0
+        R = np.exp(G[-1] - G[t])[:, None] * dST
+        for s in range(t, T):
+            R += np.exp(G[s] - G[t])[:, None] * np.outer(q64[s], do64[s])
+        assert np.allclose(got["dq"][t, 0], St @ do64[t], rtol=0, atol=1e-12)
+        want_db = (R.T @ k64[t]) @ (v64[t] - St.T @ k64[t])
+        assert abs(got["dbeta"][t, 0] - want_db) <= 1e-11 * max(1.0, abs(want_db))
+        want_dg = np.exp(G[-1]) * np.sum(S0 * dST, axis=1)
+        for s in range(t, T):
+            want_dg += np.exp(G[s]) * q64[s] * (S0 @ do64[s])
+        assert np.allclose(got["dg"][t, 0], want_dg, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(got["dk"])) == 0.0 and np.max(np.abs(got["dv"])) == 0.0
+    want_ds0 = np.exp(G[-1])[:, None] * dST
+    for s in range(T):
+        want_ds0 += np.exp(G[s])[:, None] * np.outer(q64[s], do64[s])
+    assert np.allclose(got["d_initial_state"][0, 0], want_ds0, rtol=1e-12, atol=1e-12)
+
+
+def check_bwd_homogeneity(run_bwd, seed=24):
+    """Euler's identity for maps homogeneous of degree one: o is linear in q, and
+    (o, S_T) is jointly linear in (v, S0), so with L = <dO, o> + <dS_T, S_T>,
+    <dq, q> = <dO, o> and <dv, v> + <dS0, S0> = L (packed sequences, 3 heads)."""
+    rng = np.random.default_rng(seed)
+    lens = [20, 1, 37]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, s0, do, dsT = _bwd_case(rng, sum(lens), 3, 6, 5, N=len(lens))
+    got = run_bwd(q, k, v, g, beta, do, cu_seqlens=cu, initial_state=s0, d_final_state=dsT)
+    o = np.zeros(do.shape)
+    fs = np.zeros(s0.shape)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        for h in range(3):
+            o[a:b, h], fs[n, h] = reference.explicit_matrices(q[a:b, h], k[a:b, h], v[a:b, h],
+                                                              g[a:b, h], beta[a:b, h], s0[n, h])
+    lo = np.sum(o * do)
+    L = lo + np.sum(fs * dsT)
+    assert abs(np.sum(got["dq"] * q) - lo) <= 1e-11 * max(1.0, abs(lo))
+    lhs = np.sum(got["dv"] * v) + np.sum(got["d_initial_state"] * s0)
+    assert abs(lhs - L) <= 1e-11 * max(1.0, abs(L))
+
+
+def check_bwd_empty_sequence_passes_state_gradient(run_bwd, seed=25):
+    """A sequence of length 0 leaves its state unchanged, so dS0 = dS_T for it."""
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta, s0, do, dsT = _bwd_case(rng, 5, 2, 3, 2, N=3)
+    got = run_bwd(q, k, v, g, beta, do, cu_seqlens=np.array([0, 2, 2, 5]), initial_state=s0,
+                  d_final_state=dsT)
+    assert np.array_equal(got["d_initial_state"][1], dsT[1].astype(np.float64))
+
+
+BACKWARD_CHECKS = [
+    check_bwd_finite_differences,
+    check_bwd_finite_differences_scalar_gate,
+    check_bwd_finite_differences_long,
+    check_bwd_no_write_closed_form,
+    check_bwd_homogeneity,
+    check_bwd_empty_sequence_passes_state_gradient,
+]

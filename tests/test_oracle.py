@@ -13,6 +13,11 @@ def test_pin(check):
     check(oracle.prefill)
 
 
+@pytest.mark.parametrize("check", oracle_pins.BACKWARD_CHECKS, ids=lambda f: f.__name__)
+def test_backward_pin(check):
+    check(oracle.backward)
+
+
 def test_varlen_equals_separate_runs():
     rng = np.random.default_rng(10)
     lens = [5, 17, 1, 33, 16]
@@ -191,3 +196,53 @@ def test_one_token_sequences_are_single_decode_steps():
                 + f(beta[b, h]) * np.outer(kk, f(v[b, h]))
             np.testing.assert_allclose(fs[b, h], S, rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(out[b, h], S.T @ f(q[b, h]), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk,ref", [(1, 0), (4, 3), (16, 0), (16, 8), (16, 15), (64, 32)])
+def test_chunked_backward_equals_oracle(chunk, ref):
+    """The chunk-level backward algebra (the form the GPU kernels use) equals the
+    token-by-token reverse pass, with a partial last chunk."""
+    rng = np.random.default_rng(30 + chunk + ref)
+    T, K, V = 45, 8, 6
+    q = rng.standard_normal((T, 1, K)).astype(np.float32)
+    k = (rng.standard_normal((T, 1, K)) / np.sqrt(K)).astype(np.float32)
+    v = rng.standard_normal((T, 1, V)).astype(np.float32)
+    g = (-0.3 * rng.random((T, 1, K))).astype(np.float32)
+    beta = rng.random((T, 1)).astype(np.float32)
+    do = rng.standard_normal((T, 1, V)).astype(np.float32)
+    s0 = rng.standard_normal((1, 1, K, V)).astype(np.float32)
+    dsT = rng.standard_normal((1, 1, K, V)).astype(np.float32)
+    want = oracle.backward(q, k, v, g, beta, do, initial_state=s0, d_final_state=dsT)
+    got = reference.chunked_backward(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], do[:, 0],
+                                     s0[0, 0], dsT[0, 0], chunk=chunk, ref=ref)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.max(np.abs(got[name] - want[name][:, 0])) <= 1e-12, name
+    assert np.max(np.abs(got["dS0"] - want["d_initial_state"][0, 0])) <= 1e-12
+
+
+def test_backward_varlen_and_head_subset():
+    """Packed sequences equal separate runs; a head subset equals the full run's rows."""
+    rng = np.random.default_rng(31)
+    lens = [5, 17, 0, 33]
+    T, H, K, V = sum(lens), 3, 6, 5
+    q = rng.standard_normal((T, H, K)).astype(np.float32)
+    k = (rng.standard_normal((T, H, K)) / np.sqrt(K)).astype(np.float32)
+    v = rng.standard_normal((T, H, V)).astype(np.float32)
+    g = (-0.2 * rng.random((T, H, K))).astype(np.float32)
+    beta = rng.random((T, H)).astype(np.float32)
+    do = rng.standard_normal((T, H, V)).astype(np.float32)
+    s0 = rng.standard_normal((len(lens), H, K, V)).astype(np.float32)
+    dsT = rng.standard_normal((len(lens), H, K, V)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    full = oracle.backward(q, k, v, g, beta, do, cu_seqlens=cu, initial_state=s0, d_final_state=dsT)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        one = oracle.backward(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], do[a:b],
+                              initial_state=s0[n:n + 1], d_final_state=dsT[n:n + 1])
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert np.array_equal(one[name], full[name][a:b])
+        assert np.array_equal(one["d_initial_state"][0], full["d_initial_state"][n])
+    sub = oracle.backward(q, k, v, g, beta, do, cu_seqlens=cu, initial_state=s0, d_final_state=dsT,
+                          heads=[2, 0])
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.array_equal(sub[name], full[name][:, [2, 0]])

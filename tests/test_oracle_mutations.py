@@ -15,6 +15,19 @@ from tests import oracle_pins
 SRC = os.path.join(os.path.dirname(kda_oracle.__file__), "kda_oracle.c")
 
 
+# The backward code follows the forward in the file; each set of mutations edits
+# its own part only.
+_SPLIT = "/*\n * Backward (reverse mode)"
+
+
+def _in_part(backward, edit):
+    def f(text):
+        i = text.index(_SPLIT)
+        head, tail = text[:i], text[i:]
+        return head + edit(tail) if backward else edit(head) + tail
+    return f
+
+
 def _replace(old, new):
     def f(text):
         assert text.count(old) == 1, old
@@ -66,10 +79,55 @@ MUTATIONS = {
 }
 
 
+# Slips in the reverse pass (the forward code above stays intact in these copies).
+BACKWARD_MUTATIONS = {
+    "b_no_output_outer": _replace("dS[c * V + j] += (double)qt[c] * (double)dot[j];", "(void)0;"),
+    "b_dq_from_previous_state": _replace("acc += Snew[c * V + j] * (double)dot[j];",
+                                         "acc += Sprev[c * V + j] * (double)dot[j];"),
+    "b_dk_without_write_term": _replace("acc += dS[c * V + j] * delta[j];", "acc += 0.0;"),
+    "b_dk_without_predict_term": _replace("dk_t[c] += acc;", "(void)acc;"),
+    "b_dbeta_sign": _replace("acc += ddelta[j] * ((double)vt[j] - pred[j]);",
+                             "acc += ddelta[j] * ((double)vt[j] + pred[j]);"),
+    "b_dv_without_beta": _replace("dv_t[j] = bt * ddelta[j];", "dv_t[j] = ddelta[j];"),
+    "b_dpred_sign": _replace("dpred[j] = -bt * ddelta[j];", "dpred[j] = bt * ddelta[j];"),
+    "b_dg_on_undecayed_state": _replace("acc += dS[c * V + j] * Sd[c * V + j];",
+                                        "acc += dS[c * V + j] * Sprev[c * V + j];"),
+    "b_no_decay_of_gradient": _replace("dS[c * V + j] *= alpha;", "(void)alpha;"),
+    "b_ddelta_with_query": _replace("acc += dS[c * V + j] * (double)kt[c];",
+                                    "acc += dS[c * V + j] * (double)qt[c];"),
+    "b_state_gradient_skips_predict": _replace("dS[c * V + j] += (double)kt[c] * dpred[j];", "(void)0;"),
+    "b_decay_before_predict": _swap("b_predict", "b_decay"),
+    "b_checkpoint_off_by_one": _replace("memcpy(blk, ck + b * KV, KV * sizeof(double));",
+                                        "memcpy(blk, ck + (b > 0 ? b - 1 : 0) * KV, KV * sizeof(double));"),
+    "b_ignore_final_state_gradient": _replace("dS[i] = dsT ? (double)dsT[i] : 0.0;", "dS[i] = 0.0;"),
+}
+
+
+def _build_copy(tmp_path, name, text):
+    src = tmp_path / f"mut_{name}.c"
+    src.write_text(text)
+    return kda_oracle.build(str(src), str(tmp_path / f"libmut_{name}.so"))
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_pins_catch_mutation(name, tmp_path):
+    text = open(SRC).read()
+    mutated = _in_part(True, BACKWARD_MUTATIONS[name])(text)
+    assert mutated != text
+    run_bwd = functools.partial(oracle.backward, lib_path=_build_copy(tmp_path, name, mutated))
+    caught = []
+    for check in oracle_pins.BACKWARD_CHECKS:
+        try:
+            check(run_bwd)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"mutation {name} passed every backward pin"
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_mutation(name, tmp_path):
     text = open(SRC).read()
-    mutated = MUTATIONS[name](text)
+    mutated = _in_part(False, MUTATIONS[name])(text)
     assert mutated != text
     src = tmp_path / f"mut_{name}.c"
     src.write_text(mutated)
@@ -91,3 +149,6 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
     run = functools.partial(oracle.prefill, lib_path=lib)
     for check in oracle_pins.ALL_CHECKS:
         check(run)
+    run_bwd = functools.partial(oracle.backward, lib_path=lib)
+    for check in oracle_pins.BACKWARD_CHECKS:
+        check(run_bwd)
