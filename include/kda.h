@@ -144,6 +144,44 @@ int kda_chunk_prefill_fused(const void *q, const void *k, const void *v, const f
 int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                     float *state, void *out, const kda_dims_t *dims, void *stream);
 
+/* Workspace bytes for kda_chunk_prefill_backward with these dims (0 if invalid or
+ * unsupported). Larger than the forward's: it also holds every chunk's start state
+ * and end-state gradient (bf16, 32 KiB each per (chunk, head)). */
+size_t kda_backward_workspace_bytes(const kda_dims_t *dims);
+
+/* Backward of kda_chunk_prefill for training: the gradients of
+ *     L = sum_t <d_out_t, out_t> + sum_n <d_final_state_n, S_n>
+ * with respect to q, k, v, g, beta and initial_state, for the recurrence the
+ * forward computes (S <- Diag(exp(g_t)) S, S <- S + beta_t k_t (v_t - S^T k_t)^T,
+ * out_t = S^T q_t). The pages describe only the forward kernel, and say that the
+ * released libraries ran Kimi K3's training as well as its inference (tech-noisy.com,
+ * section "Moonshot AIが公開した3本のライブラリ"); the gradients here are the plain
+ * derivatives of that recurrence, formed
+ * chunk by chunk (16 tokens) like the forward: the forward is recomputed to obtain
+ * each chunk's start state, a reverse pass over the chunks carries the state
+ * gradient, and a token-parallel pass forms the per-token gradients.
+ * dims, cu_seqlens, q, k, v, g, beta, initial_state: as kda_chunk_prefill (bf16 io,
+ *       K = V = 128 only; KDA_ERR_UNSUPPORTED otherwise).
+ * d_out [T, H, V] bf16; d_final_state [N, H, K, V] fp32 or NULL (zero).
+ * Outputs (written, never read): dq, dk [T, H, K] and dv [T, H, V] bf16 (rounded to
+ *       nearest even); dg fp32 with g's shape ([T, H, K], or [T, H] for a scalar gate:
+ *       the sum over the key channels); dbeta [T, H] fp32; d_initial_state
+ *       [N, H, K, V] fp32 or NULL (not computed).
+ * Arithmetic: fp32 accumulation with bf16 MFMA operands; chunk states and state
+ * gradients are held as bf16 between the passes.
+ * workspace: device memory of at least kda_backward_workspace_bytes(dims) bytes, owned
+ * by the caller; no other call may use it until this one has completed on `stream`.
+ * Returns KDA_OK or an error status as kda_chunk_prefill (nothing is enqueued on an
+ * argument error). Outputs must not alias inputs or each other. */
+int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens,
+                               const float *initial_state, const void *d_out,
+                               const float *d_final_state, void *dq, void *dk, void *dv,
+                               float *dg, float *dbeta, float *d_initial_state,
+                               const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);
 

@@ -23,6 +23,8 @@ SOURCES = [
     "kda_inter_bf16.hip",
     "kda_f32.hip",
     "kda_decode.hip",
+    "kda_state_grad_bf16.hip",
+    "kda_grad_bf16.hip",
 ]
 
 ARCH = "gfx950"

@@ -76,6 +76,18 @@ int make_geometry(const kda_dims_t *d, Geometry *g) {
     return KDA_OK;
 }
 
+int make_backward_geometry(const kda_dims_t *d, Geometry *g) {
+    const int st = make_geometry(d, g);
+    if (st != KDA_OK) return st;
+    if (g->io != KDA_IO_BF16) return KDA_ERR_UNSUPPORTED;
+    const size_t per = (size_t)g->max_chunks * (size_t)g->H;
+    g->off_brecords = align_up(g->total_bytes);
+    g->off_states = align_up(g->off_brecords + per * kBRecBytes);
+    g->off_dstates = align_up(g->off_states + per * kStateBytesBf16);
+    g->backward_bytes = g->off_dstates + per * kStateBytesBf16;
+    return KDA_OK;
+}
+
 }  // namespace kda
 
 using kda::Geometry;
@@ -187,6 +199,52 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *g,
                                                  dims->num_heads, dims->io_dtype,
                                                  dims->gate_kind == KDA_GATE_SCALAR,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t kda_backward_workspace_bytes(const kda_dims_t *dims) {
+    Geometry geo;
+    if (kda::make_backward_geometry(dims, &geo) != KDA_OK) return 0;
+    return geo.backward_bytes;
+}
+
+int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                               const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                               const float *d_final_state, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                               float *d_initial_state, const kda_dims_t *dims, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = kda::make_backward_geometry(dims, &geo);
+    if (st != KDA_OK) return st;
+    if (cu_seqlens == nullptr && dims->num_seqs != 1) return KDA_ERR_ARG;
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < geo.backward_bytes) return KDA_ERR_WORKSPACE;
+    if (!kda::aligned16(workspace)) return KDA_ERR_ALIGN;
+    if (geo.T > 0) {
+        st = kda::check_pointers({q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta},
+                                 {initial_state, d_final_state, d_initial_state});
+    } else {
+        st = kda::check_pointers({}, {q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta, initial_state,
+                                      d_final_state, d_initial_state});
+    }
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cu_seqlens != nullptr) {
+        st = kda::launch_status(kda::launch_chunk_table(cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    if (geo.T > 0) {
+        // chunk factors in both layouts, then the forward again for every chunk's start state
+        st = kda::launch_status(kda::launch_intra_bf16_bwd(q, k, g, beta, cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+        st = kda::launch_status(kda::launch_inter_bf16_states(v, cu_seqlens, initial_state, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    // the reverse pass also carries d_final_state through empty sequences
+    st = kda::launch_status(
+        kda::launch_state_grad_bf16(d_out, cu_seqlens, d_final_state, d_initial_state, geo, workspace, s));
+    if (st != KDA_OK || geo.T == 0) return st;
+    return kda::launch_status(kda::launch_grad_bf16(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta,
+                                                    geo, workspace, s));
 }
 
 const char *kda_status_string(int status) {

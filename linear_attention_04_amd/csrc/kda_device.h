@@ -84,6 +84,22 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, true));
 }
 
+// DPP: value of lane (l + N) within the same 16-lane row, or 0 where that lane is
+// outside the row.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, false));
+}
+
+// Inclusive suffix sum over the 16 lanes of each row (lane c gets x_c + ... + x_15).
+__device__ __forceinline__ float row_suffix_sum(float x) {
+    x += row_shl<1>(x);
+    x += row_shl<2>(x);
+    x += row_shl<4>(x);
+    x += row_shl<8>(x);
+    return x;
+}
+
 // Inclusive prefix sum over the 16 lanes of each row (lane c gets x_0 + ... + x_c).
 __device__ __forceinline__ float row_inclusive_sum(float x) {
     x += row_shr<1>(x);

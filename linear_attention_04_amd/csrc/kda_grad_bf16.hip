@@ -1,0 +1,496 @@
+// kda_grad_bf16.hip -- token-parallel gradient kernel of the backward pass, bf16 io,
+// K = V = 128.
+//
+// One wave per (16-token chunk, head), independent of every other wave. Inputs: the
+// chunk's q, k, v, g, beta, d_out, its start state S0 (from the recomputed forward)
+// and the gradient R reaching its end state (from the reverse pass), both bf16
+// fragments. With the chunk factors recomputed as in the intra-chunk kernel
+// (G, A~ = K^ K~^T, A = diag(beta) A~, P, T = (I + A)^-1, T' = T diag(beta), K+, Q+, K^d,
+// gamma; K^ = k exp(G - G_ref), Q^ = q exp(G - G_ref), K~ = k exp(G_ref - G)):
+//   U = V - K+ S0,  Delta = T' U,  dDelta = P^T dO + K^d R,  dU = T'^T dDelta = dv,
+//   dQ+ = dO S0^T,  dK+ = -dU S0^T,  dK^d = Delta R^T,  dgamma = rowsum(R * S0),
+//   dP = tril(dO Delta^T),  dT' = dDelta U^T,
+//   dbeta = colsum(dT' * T) + rowsum(dA * A~),  dT = dT' diag(beta),
+//   dA = -tril(T^T dT T^T, -1),  dA~ = diag(beta) dA,
+//   dK^ = dA~ K~,  dK~ = dA~^T K^ + dP^T Q^,  dQ^ = dP K~,
+// and then dq, dk and the running-gate gradient dG from the products that formed
+// each factor; dg is the suffix sum of dG over the chunk, with the chunk-end gate
+// G_C's gradient (through K^d and gamma) added at the last token.
+//
+// Layouts. "Row layout": lane (c, grp) = (lane % 16, lane / 16) holds token c and
+// channels 16j + 4grp + i (element 4j + i); "slab" s of it is j = 2s, 2s + 1 (eight
+// bf16, the 16x16x32 operand that matches the state fragments' key order). Products
+// over the 128 keys take the state fragments as stored. Products over the 128 value
+// columns need the state with keys across lanes: a 16x16x32 MFMA against a 0/1
+// selection matrix moves a fragment's 16 keys of one half across lanes, exactly (the
+// values are bf16 and the accumulator fp32), and a 16x16x16 MFMA against the identity
+// turns a token-per-lane tile into a column-per-lane tile the same way. Every layout
+// change in this kernel is such an exact MFMA; LDS holds only the 16 x 16 matrices.
+#include "kda_chunks.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int KD = 128;
+constexpr int VD = 128;
+constexpr int kWaves = 4;
+
+// One wave's 16 x 16 matrices, row-major.
+struct alignas(16) GradLds {
+    float a[256];    // A = diag(beta) A~, strictly lower (the forward substitution)
+    float at[256];   // A~
+    float t[256];    // T = (I + A)^-1
+    float tb[256];   // T' = T diag(beta)
+    float dt[256];   // dT = dT' diag(beta)
+    float y[256];    // Y = dT T^T
+    float dat[256];  // dA~
+    float dp[256];   // dP (i <= r)
+    float beta[16];
+};
+
+__device__ __forceinline__ void wave_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+__device__ __forceinline__ bf16x8 dup8(bf16x4 a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 bf16x4_to_f32(bf16x4 x) {
+    return f32x4{from_bf16(x[0]), from_bf16(x[1]), from_bf16(x[2]), from_bf16(x[3])};
+}
+
+// 16 x 16 fp32 matrix entries (four per lane) split into two bf16 terms, each
+// duplicated over both halves of the 32-long reduction: [M_hi; M_hi] and [M_lo; M_lo].
+struct SplitDup {
+    bf16x8 hi, lo;
+};
+__device__ __forceinline__ SplitDup split_dup(f32x4 m) {
+    bf16x4 h, l;
+    split_bf16x4(m, h, l);
+    return SplitDup{dup8(h), dup8(l)};
+}
+// [M_hi | M_lo] over the two halves of the reduction.
+__device__ __forceinline__ bf16x8 split_cat(f32x4 m) {
+    bf16x4 h, l;
+    split_bf16x4(m, h, l);
+    return cat8(h, l);
+}
+
+template <bool SCALAR_GATE>
+__global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const __bf16 *__restrict__ dout,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ chunk_seq,
+    int64_t T, int H, int N, int64_t max_chunks, const char *__restrict__ states, const char *__restrict__ dstates,
+    __bf16 *__restrict__ dq, __bf16 *__restrict__ dk, __bf16 *__restrict__ dv, float *__restrict__ dg,
+    float *__restrict__ dbeta) {
+    __shared__ GradLds lds_all[kWaves];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, grp = lane >> 4;
+    const int head_groups = (H + kWaves - 1) / kWaves;
+    const int64_t chunk = blockIdx.x / head_groups;
+    const int h = (int)(blockIdx.x - chunk * head_groups) * kWaves + wave;
+    if (h >= H) return;  // waves are independent
+    int64_t start;
+    int len;
+    chunk_span(cu, chunk_off, chunk_seq, chunk, T, N, max_chunks, start, len);
+    if (len == 0) return;
+    GradLds &L = lds_all[wave];
+    const bool row_ok = c < len;
+    const int64_t tok = start + c;
+    const size_t krow = ((size_t)(row_ok ? tok : start) * H + h) * KD;  // q, k, g, dq, dk, dg row of token c
+    const size_t vrow = ((size_t)(row_ok ? tok : start) * H + h) * VD;  // v, d_out, dv row
+    const size_t hc = (size_t)h * max_chunks + chunk;
+    const char *S0 = states + hc * kStateBytesBf16 + lane * 16;
+    const char *Rs = dstates + hc * kStateBytesBf16 + lane * 16;
+    const float b = row_ok ? beta[(size_t)tok * H + h] : 0.f;
+
+    // exact 0/1 operands: I4 (16x16x16 B operand, identity) and Isel[hf] (16x16x32 B
+    // operand taking the keys 16 hf .. 16 hf + 15 of a state fragment's 32)
+    s16x4 I4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) I4[j] = (4 * grp + j == c) ? (short)0x3F80 : (short)0;
+    bf16x8 Isel[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            Isel[hf][e] = to_bf16(((e >> 2) == hf && 4 * grp + (e & 3) == c) ? 1.f : 0.f);
+
+    // ================= 1. chunk factors (as the intra-chunk kernel) =================
+    bf16x8 kps[4], kds[4];  // K+ and K^d slabs (row layout, bf16)
+    f32x4 pcol;             // P[4grp + i][c] (i <= r kept)
+    {
+        float kr[32], qr[32], G[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint2 qw = make_uint2(0u, 0u), kw = make_uint2(0u, 0u);
+            float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row_ok) {
+                qw = *reinterpret_cast<const uint2 *>(q + krow + 16 * j + 4 * grp);
+                kw = *reinterpret_cast<const uint2 *>(k + krow + 16 * j + 4 * grp);
+                if (!SCALAR_GATE) gv = *reinterpret_cast<const float4 *>(g + krow + 16 * j + 4 * grp);
+            }
+            qr[4 * j] = __uint_as_float(qw.x << 16);
+            qr[4 * j + 1] = __uint_as_float(qw.x & 0xffff0000u);
+            qr[4 * j + 2] = __uint_as_float(qw.y << 16);
+            qr[4 * j + 3] = __uint_as_float(qw.y & 0xffff0000u);
+            kr[4 * j] = __uint_as_float(kw.x << 16);
+            kr[4 * j + 1] = __uint_as_float(kw.x & 0xffff0000u);
+            kr[4 * j + 2] = __uint_as_float(kw.y << 16);
+            kr[4 * j + 3] = __uint_as_float(kw.y & 0xffff0000u);
+            G[4 * j] = gv.x;
+            G[4 * j + 1] = gv.y;
+            G[4 * j + 2] = gv.z;
+            G[4 * j + 3] = gv.w;
+        }
+        if (SCALAR_GATE) {
+            const float gs = row_inclusive_sum(row_ok ? g[(size_t)tok * H + h] : 0.f);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) G[e] = gs;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) G[e] = row_inclusive_sum(G[e]);
+        }
+
+        // A~ and P (two-term bf16 splits of both factors); K^d and K+ slabs
+        f32x4 acc_a = zero4(), acc_p = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4], kdw[4], kpw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = 8 * s + 2 * u;
+                const float d0 = G[e] - row_bcast<7>(G[e]), d1 = G[e + 1] - row_bcast<7>(G[e + 1]);
+                const float up0 = __expf(d0), up1 = __expf(d1);
+                const float dn0 = __expf(-d0), dn1 = __expf(-d1);
+                kdw[u] = pack_bf16x2(kr[e] * (dn0 * row_bcast<15>(up0)), kr[e + 1] * (dn1 * row_bcast<15>(up1)));
+                kpw[u] = pack_bf16x2(kr[e] * __expf(G[e]), kr[e + 1] * __expf(G[e + 1]));
+                split_pair(kr[e] * up0, kr[e + 1] * up1, khh[u], khl[u]);
+                split_pair(qr[e] * up0, qr[e + 1] * up1, qhh[u], qhl[u]);
+                split_pair(kr[e] * dn0, kr[e + 1] * dn1, kbh[u], kbl[u]);
+            }
+            kds[s] = __builtin_bit_cast(bf16x8, make_uint4(kdw[0], kdw[1], kdw[2], kdw[3]));
+            kps[s] = __builtin_bit_cast(bf16x8, make_uint4(kpw[0], kpw[1], kpw[2], kpw[3]));
+            const bf16x8 vkhh = __builtin_bit_cast(bf16x8, make_uint4(khh[0], khh[1], khh[2], khh[3]));
+            const bf16x8 vkhl = __builtin_bit_cast(bf16x8, make_uint4(khl[0], khl[1], khl[2], khl[3]));
+            const bf16x8 vkbh = __builtin_bit_cast(bf16x8, make_uint4(kbh[0], kbh[1], kbh[2], kbh[3]));
+            const bf16x8 vkbl = __builtin_bit_cast(bf16x8, make_uint4(kbl[0], kbl[1], kbl[2], kbl[3]));
+            const bf16x8 vqhh = __builtin_bit_cast(bf16x8, make_uint4(qhh[0], qhh[1], qhh[2], qhh[3]));
+            const bf16x8 vqhl = __builtin_bit_cast(bf16x8, make_uint4(qhl[0], qhl[1], qhl[2], qhl[3]));
+            acc_a = mfma_16x16x32(vkhh, vkbh, acc_a);
+            acc_a = mfma_16x16x32(vkhl, vkbh, acc_a);
+            acc_a = mfma_16x16x32(vkhh, vkbl, acc_a);
+            acc_p = mfma_16x16x32(vqhh, vkbh, acc_p);
+            acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
+            acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
+        }
+        // acc_a[i] = A~[4grp + i][c], acc_p[i] = P[4grp + i][c]
+        if (grp == 0) L.beta[c] = b;
+        wave_sync();
+        const f32x4 brow = *reinterpret_cast<const f32x4 *>(&L.beta[4 * grp]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * grp + i;
+            L.at[r * 16 + c] = acc_a[i];
+            L.a[r * 16 + c] = (c < r) ? brow[i] * acc_a[i] : 0.f;
+            pcol[i] = (c <= r) ? acc_p[i] : 0.f;
+        }
+        wave_sync();
+    }
+    // T = (I + A)^-1 by forward substitution, lane column c; T' = T diag(beta)
+    {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= L.a[r * 16 + i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float xi = grp == 0 ? x[i] : (grp == 1 ? x[4 + i] : (grp == 2 ? x[8 + i] : x[12 + i]));
+            L.t[(4 * grp + i) * 16 + c] = xi;
+            L.tb[(4 * grp + i) * 16 + c] = xi * b;
+        }
+    }
+    wave_sync();
+    // T' row c and column c, [hi | lo]; P column c, [hi | lo]
+    const bf16x8 tbr = split_cat(*reinterpret_cast<const f32x4 *>(&L.tb[c * 16 + 4 * grp]));
+    f32x4 tcol;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tcol[i] = L.tb[(4 * grp + i) * 16 + c];
+    const bf16x8 tbc = split_cat(tcol);
+    const bf16x8 pc = split_cat(pcol);
+
+    // ================= 2. products over the keys, per 32-column value slab =================
+    f32x4 dpa = zero4(), dtpa = zero4();  // dP[4grp + i][c], dT'[4grp + i][c]
+    bf16x8 delf[4], duf[4];               // Delta and dU per slab (token c, slab's 8 columns)
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+        f32x4 ksv[2], kst[2], xv[2], xt[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ksv[t] = kst[t] = xv[t] = xt[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int off = ((2 * p + t) * 4 + ks) * 1024;
+                const bf16x8 s0f = *reinterpret_cast<const bf16x8 *>(S0 + off);
+                const bf16x8 rf = *reinterpret_cast<const bf16x8 *>(Rs + off);
+                ksv[t] = mfma_16x16x32(kps[ks], s0f, ksv[t]);  // K+ S0, column per lane
+                kst[t] = mfma_16x16x32(s0f, kps[ks], kst[t]);  // the same, token per lane
+                xv[t] = mfma_16x16x32(kds[ks], rf, xv[t]);     // K^d R
+                xt[t] = mfma_16x16x32(rf, kds[ks], xt[t]);
+            }
+        }
+        bf16x4 dtok[2], utok[2], deltok[2], ddtok[2], dutok[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = 16 * (2 * p + t) + 4 * grp;
+            bf16x4 vt4 = {}, dt4 = {};
+            if (row_ok) {
+                vt4 = *reinterpret_cast<const bf16x4 *>(v + vrow + col);
+                dt4 = *reinterpret_cast<const bf16x4 *>(dout + vrow + col);
+            }
+            // column per lane: V[4grp + i][16t' + c], dO likewise (identity MFMA, exact)
+            const f32x4 vcol = mfma_16x16x16(as_s16x4(vt4), I4, zero4());
+            const f32x4 dcol = mfma_16x16x16(as_s16x4(dt4), I4, zero4());
+            const f32x4 ucol = vcol - ksv[t];                 // U, column per lane
+            const f32x4 utk = bf16x4_to_f32(vt4) - kst[t];    // U, token per lane
+            bf16x4 uh, ul;
+            split_bf16x4(ucol, uh, ul);
+            // Delta^T = U^T T'^T: token per lane
+            f32x4 del = mfma_16x16x32(dup8(uh), tbr, zero4());
+            del = mfma_16x16x32(dup8(ul), tbr, del);
+            const bf16x8 dcd = dup8(to_bf16x4(dcol));  // dO column tile (exact)
+            // dDelta = P^T dO + K^d R, column per lane and token per lane
+            const f32x4 ddc = mfma_16x16x32(pc, dcd, xv[t]);
+            const f32x4 ddt = mfma_16x16x32(dcd, pc, xt[t]);
+            // dU^T = dDelta^T T': token per lane
+            bf16x4 dh, dl;
+            split_bf16x4(ddc, dh, dl);
+            f32x4 du = mfma_16x16x32(dup8(dh), tbc, zero4());
+            du = mfma_16x16x32(dup8(dl), tbc, du);
+            dtok[t] = dt4;
+            utok[t] = to_bf16x4(utk);
+            deltok[t] = to_bf16x4(del);
+            ddtok[t] = to_bf16x4(ddt);
+            dutok[t] = to_bf16x4(du);
+            if (row_ok) *reinterpret_cast<bf16x4 *>(dv + vrow + col) = dutok[t];
+        }
+        const bf16x8 df = cat8(dtok[0], dtok[1]);
+        delf[p] = cat8(deltok[0], deltok[1]);
+        duf[p] = cat8(dutok[0], dutok[1]);
+        dpa = mfma_16x16x32(df, delf[p], dpa);                                 // dO Delta^T
+        dtpa = mfma_16x16x32(cat8(ddtok[0], ddtok[1]), cat8(utok[0], utok[1]), dtpa);  // dDelta U^T
+    }
+
+    // ================= 3. the 16 x 16 backward =================
+    float dbeta_c;
+    SplitDup m_darow, m_dacol, m_dprow, m_dpcol;
+    {
+        f32x4 dpm, tcolT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * grp + i;
+            dpm[i] = (c <= r) ? dpa[i] : 0.f;
+            tcolT[i] = L.t[r * 16 + c];
+            L.dt[r * 16 + c] = dtpa[i] * b;  // dT[r][c] = dT'[r][c] beta_c
+            L.dp[r * 16 + c] = dpm[i];
+        }
+        float db1 = dtpa[0] * tcolT[0] + dtpa[1] * tcolT[1] + dtpa[2] * tcolT[2] + dtpa[3] * tcolT[3];
+        db1 += __shfl_xor(db1, 16, 64);
+        db1 += __shfl_xor(db1, 32, 64);
+        wave_sync();
+        // Y[c][4grp + j] = sum_m dT[c][m] T[4grp + j][m]
+        f32x4 yv = zero4();
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const f32x4 dtr = *reinterpret_cast<const f32x4 *>(&L.dt[c * 16 + 4 * m4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 trow = *reinterpret_cast<const f32x4 *>(&L.t[(4 * grp + j) * 16 + 4 * m4]);
+                yv[j] += dtr[0] * trow[0] + dtr[1] * trow[1] + dtr[2] * trow[2] + dtr[3] * trow[3];
+            }
+        }
+        *reinterpret_cast<f32x4 *>(&L.y[c * 16 + 4 * grp]) = yv;
+        wave_sync();
+        // dA[c][4grp + j] = -sum_m T[m][c] Y[m][4grp + j], strictly lower
+        f32x4 da = zero4();
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const float tmc = L.t[m * 16 + c];
+            da -= tmc * *reinterpret_cast<const f32x4 *>(&L.y[m * 16 + 4 * grp]);
+        }
+        const f32x4 atr = *reinterpret_cast<const f32x4 *>(&L.at[c * 16 + 4 * grp]);
+        float db2 = 0.f;
+        f32x4 dat;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            da[j] = (4 * grp + j < c) ? da[j] : 0.f;
+            db2 += da[j] * atr[j];
+            dat[j] = b * da[j];
+        }
+        db2 += __shfl_xor(db2, 16, 64);
+        db2 += __shfl_xor(db2, 32, 64);
+        dbeta_c = db1 + db2;
+        *reinterpret_cast<f32x4 *>(&L.dat[c * 16 + 4 * grp]) = dat;
+        wave_sync();
+        f32x4 dacol;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dacol[j] = L.dat[(4 * grp + j) * 16 + c];
+        m_darow = split_dup(dat);
+        m_dacol = split_dup(dacol);
+        m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
+        m_dpcol = split_dup(dpm);
+    }
+    if (grp == 0 && row_ok) dbeta[(size_t)tok * H + h] = dbeta_c;
+
+    // ================= 4. per 32-key slab: products over the values, then dq, dk, dg =================
+    float dgs = 0.f;  // scalar gate: sum of dg over this lane's channels
+#pragma unroll 1
+    for (int ks = 0; ks < 4; ++ks) {
+        f32x4 dqp[2], dkp[2], dkd[2];
+        float dgam[2] = {0.f, 0.f};  // key 32ks + 16hf + c, this lane group's columns
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) dqp[hf] = dkp[hf] = dkd[hf] = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const bf16x8 sa = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p) * 4 + ks) * 1024);
+            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p + 1) * 4 + ks) * 1024);
+            const bf16x8 ra = *reinterpret_cast<const bf16x8 *>(Rs + ((2 * p) * 4 + ks) * 1024);
+            const bf16x8 rb = *reinterpret_cast<const bf16x8 *>(Rs + ((2 * p + 1) * 4 + ks) * 1024);
+            bf16x4 d0 = {}, d1 = {};
+            if (row_ok) {
+                d0 = *reinterpret_cast<const bf16x4 *>(dout + vrow + 32 * p + 4 * grp);
+                d1 = *reinterpret_cast<const bf16x4 *>(dout + vrow + 32 * p + 16 + 4 * grp);
+            }
+            const bf16x8 df = cat8(d0, d1);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                // key 32ks + 16hf + c across lanes, columns 32p + 4grp + i and 32p + 16 + 4grp + i
+                const f32x4 sta = mfma_16x16x32(sa, Isel[hf], zero4());
+                const f32x4 stb = mfma_16x16x32(sb, Isel[hf], zero4());
+                const f32x4 rta = mfma_16x16x32(ra, Isel[hf], zero4());
+                const f32x4 rtb = mfma_16x16x32(rb, Isel[hf], zero4());
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dgam[hf] += sta[i] * rta[i] + stb[i] * rtb[i];
+                const bf16x8 st = cat8(to_bf16x4(sta), to_bf16x4(stb));
+                const bf16x8 rt = cat8(to_bf16x4(rta), to_bf16x4(rtb));
+                dqp[hf] = mfma_16x16x32(st, df, dqp[hf]);      // (dO S0^T)^T
+                dkp[hf] = mfma_16x16x32(st, duf[p], dkp[hf]);  // (dU S0^T)^T
+                dkd[hf] = mfma_16x16x32(rt, delf[p], dkd[hf]); // (Delta R^T)^T
+            }
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int kt = 2 * ks + hf;  // channels 16kt + 4grp + i of token c
+            const size_t kc = krow + 16 * kt + 4 * grp;
+            f32x4 kk = zero4(), qq = zero4(), G = zero4();
+            if (row_ok) {
+                kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(k + kc));
+                qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(q + kc));
+                if (SCALAR_GATE) {
+                    const float gs = g[(size_t)tok * H + h];
+                    G = f32x4{gs, gs, gs, gs};
+                } else {
+                    const float4 gv = *reinterpret_cast<const float4 *>(g + kc);
+                    G = f32x4{gv.x, gv.y, gv.z, gv.w};
+                }
+            }
+            f32x4 up, dn, eg, ed, gam, khat, qhat, krev;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                G[i] = row_inclusive_sum(G[i]);
+                const float d = G[i] - row_bcast<7>(G[i]);
+                up[i] = __expf(d);
+                dn[i] = __expf(-d);
+                eg[i] = __expf(G[i]);
+                ed[i] = dn[i] * row_bcast<15>(up[i]);
+                gam[i] = row_bcast<15>(eg[i]);
+                khat[i] = kk[i] * up[i];
+                qhat[i] = qq[i] * up[i];
+                krev[i] = kk[i] * dn[i];
+            }
+            // channel per lane, [hi | lo] over tokens 4grp .. + 3 (identity MFMAs, exact)
+            auto chan_major = [&](f32x4 x) {
+                bf16x4 xh, xl;
+                split_bf16x4(x, xh, xl);
+                const f32x4 th = mfma_16x16x16(as_s16x4(xh), I4, zero4());
+                const f32x4 tl = mfma_16x16x16(as_s16x4(xl), I4, zero4());
+                return cat8(to_bf16x4(th), to_bf16x4(tl));
+            };
+            const bf16x8 krev_c = chan_major(krev), khat_c = chan_major(khat), qhat_c = chan_major(qhat);
+            f32x4 dkhat = mfma_16x16x32(krev_c, m_darow.hi, zero4());
+            dkhat = mfma_16x16x32(krev_c, m_darow.lo, dkhat);
+            f32x4 dkrev = mfma_16x16x32(khat_c, m_dacol.hi, zero4());
+            dkrev = mfma_16x16x32(khat_c, m_dacol.lo, dkrev);
+            dkrev = mfma_16x16x32(qhat_c, m_dpcol.hi, dkrev);
+            dkrev = mfma_16x16x32(qhat_c, m_dpcol.lo, dkrev);
+            f32x4 dqhat = mfma_16x16x32(krev_c, m_dprow.hi, zero4());
+            dqhat = mfma_16x16x32(krev_c, m_dprow.lo, dqhat);
+
+            // dgamma for this lane's four channels: sum over the lane groups, then
+            // channel 16kt + 4grp + i sits in lane 4grp + i
+            float dgt = dgam[hf];
+            dgt += __shfl_xor(dgt, 16, 64);
+            dgt += __shfl_xor(dgt, 32, 64);
+            f32x4 dkq, dqq, dgv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float dkplus = -dkp[hf][i];
+                const float kd = kk[i] * ed[i];
+                dkq[i] = dkhat[i] * up[i] + dkrev[i] * dn[i] + dkplus * eg[i] + dkd[hf][i] * ed[i];
+                dqq[i] = dqhat[i] * up[i] + dqp[hf][i] * eg[i];
+                float dG = dkhat[i] * khat[i] - dkrev[i] * krev[i] + dqhat[i] * qhat[i] + dkplus * (kk[i] * eg[i]) +
+                           dqp[hf][i] * (qq[i] * eg[i]) - dkd[hf][i] * kd;
+                const float dgc = row_bcast<15>(row_inclusive_sum(dkd[hf][i] * kd)) +
+                                  __shfl(dgt, 4 * grp + i, 64) * gam[i];
+                if (c == len - 1) dG += dgc;
+                dgv[i] = row_suffix_sum(dG);
+            }
+            if (row_ok) {
+                *reinterpret_cast<bf16x4 *>(dk + kc) = to_bf16x4(dkq);
+                *reinterpret_cast<bf16x4 *>(dq + kc) = to_bf16x4(dqq);
+                if (SCALAR_GATE)
+                    dgs += dgv[0] + dgv[1] + dgv[2] + dgv[3];
+                else
+                    *reinterpret_cast<float4 *>(dg + kc) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
+            }
+        }
+    }
+    if (SCALAR_GATE) {
+        dgs += __shfl_xor(dgs, 16, 64);
+        dgs += __shfl_xor(dgs, 32, 64);
+        if (grp == 0 && row_ok) dg[(size_t)tok * H + h] = dgs;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grad_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *d_out, const int32_t *cu_seqlens, void *dq, void *dk, void *dv, float *dg,
+                            float *dbeta, const Geometry &geo, const void *ws, hipStream_t stream) {
+    if (geo.max_chunks == 0) return hipSuccess;
+    const char *base = static_cast<const char *>(ws);
+    const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
+    const int32_t *chunk_seq = reinterpret_cast<const int32_t *>(base + geo.off_chunk_seq);
+    const int64_t blocks = geo.max_chunks * ((geo.H + kWaves - 1) / kWaves);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    auto kern = geo.scalar_gate ? kda_grad_bf16_kernel<true> : kda_grad_bf16_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), 0, stream, static_cast<const __bf16 *>(q),
+                       static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v), g, beta,
+                       static_cast<const __bf16 *>(d_out), cu_seqlens, chunk_off, chunk_seq, geo.T, geo.H, geo.N,
+                       geo.max_chunks, base + geo.off_states, base + geo.off_dstates, static_cast<__bf16 *>(dq),
+                       static_cast<__bf16 *>(dk), static_cast<__bf16 *>(dv), dg, dbeta);
+    return hipGetLastError();
+}
+
+}  // namespace kda

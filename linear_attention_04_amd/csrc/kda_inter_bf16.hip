@@ -33,6 +33,7 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_intra_wave.h"
+#include "kda_ring.h"
 
 namespace kda {
 namespace {
@@ -41,7 +42,6 @@ constexpr int KD = 128;
 constexpr int VD = 128;
 constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // A workgroup has 2 kNW compute waves (kNW tiles of 16 value columns, two waves
 // each) and kNW producer waves. Producers stream each chunk into a ring slot of
@@ -60,44 +60,6 @@ constexpr int kSlotBytes = 16384;
 constexpr int kVOff = 15360;
 static_assert(kRecGAM == 14336 && kRecBytesBf16 == 14848, "record layout");
 
-template <int M, int I>
-__device__ __forceinline__ float gamma_of(const float2 gam) {
-    // element e = 4M + I of this lane group's permuted gamma sits in lane e >> 1, slot e & 1
-    return row_bcast<((4 * M + I) >> 1)>((I & 1) ? gam.y : gam.x);
-}
-
-template <int M>
-__device__ __forceinline__ void decay_tile(f32x4 &s, const float2 gam) {
-    s[0] *= gamma_of<M, 0>(gam);
-    s[1] *= gamma_of<M, 1>(gam);
-    s[2] *= gamma_of<M, 2>(gam);
-    s[3] *= gamma_of<M, 3>(gam);
-}
-
-// s_waitcnt vmcnt(N) without waiting on the LDS / export counters (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Wait until this (producer) wave's loads for one chunk have landed: at most
-// `later` chunks' loads, issued after that chunk's, may stay outstanding. Vector
-// memory loads complete in issue order and producers issue nothing else, so the
-// count is exact. `later` is wave-uniform and in [0, DEPTH - 2].
-template <int PER_WAVE, int DEPTH>
-__device__ __forceinline__ void wait_for_chunk(int later) {
-    static_assert(DEPTH >= 2 && DEPTH <= 8, "extend the switch");
-    switch (later) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<(DEPTH > 2 ? 1 : 0) * PER_WAVE>(); break;
-    case 2: wait_vmcnt<(DEPTH > 3 ? 2 : 0) * PER_WAVE>(); break;
-    case 3: wait_vmcnt<(DEPTH > 4 ? 3 : 0) * PER_WAVE>(); break;
-    case 4: wait_vmcnt<(DEPTH > 5 ? 4 : 0) * PER_WAVE>(); break;
-    case 5: wait_vmcnt<(DEPTH > 6 ? 5 : 0) * PER_WAVE>(); break;
-    default: wait_vmcnt<(DEPTH > 7 ? 6 : 0) * PER_WAVE>(); break;
-    }
-}
 
 // Per-lane byte offsets that stay fixed for the whole sequence.
 struct LaneOffsets {
@@ -108,12 +70,6 @@ struct LaneOffsets {
     unsigned int vrow;   // one token row of v / out in bytes (H * VD * 2)
 };
 
-// Buffer descriptor over `bytes` bytes at `base` (wave-uniform). Buffer accesses
-// are range-checked by the hardware: loads past the end return zero and stores
-// past the end are dropped, which is how rows past a short chunk are handled.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
-}
 
 // Bytes of a chunk's rows [0, len) restricted to the workgroup's 32 columns.
 __device__ __forceinline__ int tile_bytes(int len, unsigned int vrow) {
@@ -197,14 +153,14 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
     o.vv = __builtin_bit_cast(bf16x8, make_uint4(v01, v23, v01, v23));
 }
 
-// s_waitcnt lgkmcnt(0): this wave's LDS accesses have completed.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14)); }
 
 // First half of a chunk step, before the barrier: partial W S and Q~ S over this
 // wave's rows, published to the partner; then the decay of this wave's rows.
-template <int KH>
+// SAVE (the forward recomputed for a backward pass): the chunk's start state goes
+// to `sdst` as bf16 fragments (ct, 2 KH) and (ct, 2 KH + 1), and no output is formed.
+template <int KH, bool SAVE = false>
 __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f32x4 &x, f32x4 &y,
-                                             char *xchg, int lane) {
+                                             char *xchg, int lane, char *sdst = nullptr) {
     bf16x8 sb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -219,17 +175,21 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
     // eight reduction elements), so the same registers serve. Each lane then holds
     // four consecutive value columns of one token.
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if (SAVE) {
+        *reinterpret_cast<bf16x8 *>(sdst) = sb[0];
+        *reinterpret_cast<bf16x8 *>(sdst + 1024) = sb[1];
+    }
     x = mfma_16x16x32(o.w[0], sb[0], zero);
-    y = mfma_16x16x32(sb[0], o.qt[0], zero);
+    if (!SAVE) y = mfma_16x16x32(sb[0], o.qt[0], zero);
     x = mfma_16x16x32(o.w[1], sb[1], x);
-    y = mfma_16x16x32(sb[1], o.qt[1], y);
+    if (!SAVE) y = mfma_16x16x32(sb[1], o.qt[1], y);
     if (KH == 0) {
         *reinterpret_cast<f32x4 *>(xchg + lane * 16) = x;
-        y = mfma_16x16x32(o.vv, o.tv, y);  // + (M V)^T
+        if (!SAVE) y = mfma_16x16x32(o.vv, o.tv, y);  // + (M V)^T
     } else {
         x -= mfma_16x16x32(o.tv, o.vv, zero);  // - T' V
         *reinterpret_cast<f32x4 *>(xchg + 1024 + lane * 16) = x;
-        *reinterpret_cast<f32x4 *>(xchg + 2048 + lane * 16) = y;
+        if (!SAVE) *reinterpret_cast<f32x4 *>(xchg + 2048 + lane * 16) = y;
     }
     decay_tile<4 * KH + 0>(S[0], o.gam);
     decay_tile<4 * KH + 1>(S[1], o.gam);
@@ -239,11 +199,11 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
 
 // The partner half's contribution for chunk parity buffer `xchg`: half 0 takes
 // half 1's W S part (minus T' V) and output part; half 1 takes half 0's W S part.
-template <int KH>
+template <int KH, bool SAVE = false>
 __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &px, f32x4 &py) {
     if (KH == 0) {
         px = *reinterpret_cast<const f32x4 *>(xchg + 1024 + lane * 16);
-        py = *reinterpret_cast<const f32x4 *>(xchg + 2048 + lane * 16);
+        if (!SAVE) py = *reinterpret_cast<const f32x4 *>(xchg + 2048 + lane * 16);
     } else {
         px = *reinterpret_cast<const f32x4 *>(xchg + lane * 16);
     }
@@ -252,7 +212,7 @@ __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &
 // Second half, after the barrier: Delta = T' V - W S from both parts (the two
 // halves form the same sum, so they hold bitwise equal Delta), the state update of
 // this wave's rows and, on half 0, the output.
-template <int KH>
+template <int KH, bool SAVE = false>
 __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], const f32x4 &x, const f32x4 &y,
                                              const f32x4 &px, const f32x4 &py, char *ochunk, int len,
                                              const LaneOffsets &lo) {
@@ -267,7 +227,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
     }
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) S[mm] = mfma_16x16x32(o.kd[mm], db, S[mm]);  // K^d^T (Delta_hi + Delta_lo)
-    if (KH == 0) {
+    if (KH == 0 && !SAVE) {
         const f32x4 yt = y + py;
         // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
         // end of a short chunk fall outside the descriptor and are dropped
@@ -278,18 +238,14 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
     }
 }
 
-__device__ __forceinline__ void barrier() {
-    asm volatile("" ::: "memory");  // no LDS or global access moves across the barrier
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // The chunk loop of compute wave (vt, KH). Barrier B_j (j = 0 .. nchunks) is passed
 // once by every wave of the workgroup: B_j (j < nchunks) publishes chunk j's ring
 // slot, and B_{j+1} also publishes the partial products of chunk j.
-template <int KH, int DEPTH>
+template <int KH, int DEPTH, bool SAVE = false>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
-                                             char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo) {
+                                             char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
+                                             char *sdst0 = nullptr) {
     auto slot_of = [&](int64_t j) {
         return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
     };
@@ -306,12 +262,12 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, y, px, py;
         char *xc = xchg_of(j);
-        chunk_part_a<KH>(cur, S, x, y, xc, lane);
+        chunk_part_a<KH, SAVE>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * kStateBytesBf16 : nullptr);
         wait_lgkm0();  // the partial products are in LDS before the barrier
         barrier();     // B_{j+1}
-        read_partner<KH>(xc, lane, px, py);
+        read_partner<KH, SAVE>(xc, lane, px, py);
         read_ops<KH>(next, slot_of(j + 1), vt, lane);
-        chunk_part_b<KH>(cur, S, x, y, px, py, o0 + (size_t)j * chunk_rows, len_of(j), lo);
+        chunk_part_b<KH, SAVE>(cur, S, x, y, px, py, SAVE ? nullptr : o0 + (size_t)j * chunk_rows, len_of(j), lo);
     };
     HalfOps opa, opb;
     barrier();  // B_0
@@ -326,12 +282,13 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 
 // The compute waves' part of a recurrent workgroup: the state slice in, the chunk
 // loop over the LDS ring, the state slice out. Compute wave (vt, kh) owns value
-// columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63.
-template <int DEPTH>
+// columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63. SAVE: `states` points at
+// the sequence's first chunk in the [H][max_chunks] array of chunk start states.
+template <int DEPTH, bool SAVE = false>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
-                                             float *__restrict__ sT) {
+                                             float *__restrict__ sT, char *states = nullptr) {
     const int c = lane & 15, grp = lane >> 4;
     const int vt = wid >> 1, kh = wid & 1;
     lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
@@ -350,13 +307,15 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     // use sits inside the chunk loop and, since stores count on the same counter,
     // makes every chunk wait for the previous chunk's output store to complete.
     wait_vmcnt<0>();
-    char *o0 = reinterpret_cast<char *>(out) + tok_bytes;
+    char *o0 = SAVE ? nullptr : reinterpret_cast<char *>(out) + tok_bytes;  // no output when SAVE
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
     const int64_t tok_rows = sc.tok_end - sc.tok_begin;
+    // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile
+    char *sdst0 = SAVE ? states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16 : nullptr;
     if (kh == 0)
-        compute_wave<0, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
+        compute_wave<0, DEPTH, SAVE>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
     else
-        compute_wave<1, DEPTH>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo);
+        compute_wave<1, DEPTH, SAVE>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
 
     if (sT) {
 #pragma unroll
@@ -366,12 +325,14 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     }
 }
 
-template <int DEPTH>
+// SAVE: the forward recomputed for a backward pass; every chunk's start state goes to
+// `states` ([H][max_chunks] x 32 KiB fragments) and no output or final state is written.
+template <int DEPTH, bool SAVE>
 __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
-    const char *__restrict__ records) {
+    const char *__restrict__ records, char *__restrict__ states) {
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
     static_assert((DEPTH - 1) * kPerWave < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
@@ -422,10 +383,12 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
         return;
     }
 
-    compute_role<DEPTH>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
+    char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
+    compute_role<DEPTH, SAVE>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
+                              SAVE ? nullptr : sT, st);
 }
 
-template <int DEPTH>
+template <int DEPTH, bool SAVE>
 hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                   const Geometry &geo, const void *ws, hipStream_t stream) {
     const int pairs = geo.N * geo.H;
@@ -433,13 +396,14 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     const size_t lds = (size_t)DEPTH * kSlotBytes + kXchgBytes;
-    auto kern = kda_inter_bf16_kernel<DEPTH>;
+    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kWaves), lds, stream, static_cast<const unsigned short *>(v),
                        cu_seqlens, chunk_off, s0, static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N,
-                       geo.max_chunks, base + geo.off_records);
+                       geo.max_chunks, base + geo.off_records,
+                       SAVE ? const_cast<char *>(base) + geo.off_states : nullptr);
     return hipGetLastError();
 }
 
@@ -530,8 +494,16 @@ hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const flo
     // workgroups fit on a CU.
     constexpr int kCUs = 256;
     const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
-    if (blocks <= kCUs) return launch<8>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    return launch<4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    if (blocks <= kCUs) return launch<8, false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch<4, false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+}
+
+hipError_t launch_inter_bf16_states(const void *v, const int32_t *cu_seqlens, const float *s0,
+                                    const Geometry &geo, void *ws, hipStream_t stream) {
+    constexpr int kCUs = 256;
+    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
+    if (blocks <= kCUs) return launch<8, true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
+    return launch<4, true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
 }
 
 }  // namespace kda

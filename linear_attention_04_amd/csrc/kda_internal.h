@@ -27,6 +27,28 @@ constexpr int kRecMM = 13312;
 constexpr int kRecGAM = 14336;
 constexpr int kRecBytesBf16 = 14848;
 
+// bf16 backward record of one (chunk, head), written by the intra-chunk kernel next to
+// the forward record when a backward pass needs it, and read by the reverse
+// state-gradient kernel. The reverse pass multiplies by K^d where the forward
+// multiplies by W and by W^T, Q~^T where the forward multiplies by K^d^T, so the
+// same factors are stored in the other operand layouts:
+//   KD   0      [4 slabs][64 lanes][8 bf16]  K^d in the layout of W above
+//   WT   4096   [4 pairs][64 lanes][8 bf16]  W in the layout of KD above
+//   QT   8192   [4 pairs][64 lanes][8 bf16]  Q~ in the layout of KD above
+//   GAM  12288  as GAM above
+constexpr int kBRecKD = 0;
+constexpr int kBRecWT = 4096;
+constexpr int kBRecQT = 8192;
+constexpr int kBRecGAM = 12288;
+constexpr int kBRecBytes = 12800;
+
+// A 128 x 128 state (or state gradient) of one (chunk, head) in bf16, as 32 MFMA
+// fragments of 1 KiB: fragment (ct, ks) at byte ((ct * 4 + ks) * 64 + lane) * 16 holds,
+// in lane (c, grp) = (lane % 16, lane / 16), value column 16 ct + c and key rows
+// 32 ks + 4 grp + i (elements i = 0..3) and 32 ks + 16 + 4 grp + i (elements 4..7):
+// the B operand of W S in the recurrent kernel, as that kernel holds it.
+constexpr int kStateBytesBf16 = 32768;
+
 // fp32 record for head dimension K: W, QT, KD [16][K]; TB, MM [16][16]; GAM [K] (all fp32).
 constexpr size_t rec_bytes_f32(int K) { return 4u * (3u * 16u * (size_t)K + 2u * 256u + (size_t)K); }
 
@@ -40,10 +62,18 @@ struct Geometry {
     size_t off_records;      // records [H][max_chunks] (head-major: a head's chunks are contiguous)
     size_t record_bytes;
     size_t total_bytes;
+    // backward only (make_backward_geometry): backward records, chunk start states
+    // and chunk end-state gradients, each [H][max_chunks] like the records
+    size_t off_brecords;
+    size_t off_states;
+    size_t off_dstates;
+    size_t backward_bytes;
 };
 
 // Fills g from d; returns KDA_OK or a negative status (no device access).
 int make_geometry(const kda_dims_t *d, Geometry *g);
+// make_geometry plus the backward pass's workspace areas (bf16 io only).
+int make_backward_geometry(const kda_dims_t *d, Geometry *g);
 
 hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, void *ws,
                               hipStream_t stream);
@@ -52,6 +82,17 @@ hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const
                              hipStream_t stream);
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream);
+// Backward pass: records for both directions, the forward recomputed for the chunk
+// start states, the reverse state-gradient pass and the token-parallel gradients.
+hipError_t launch_intra_bf16_bwd(const void *q, const void *k, const float *g, const float *beta,
+                                 const int32_t *cu_seqlens, const Geometry &geo, void *ws, hipStream_t stream);
+hipError_t launch_inter_bf16_states(const void *v, const int32_t *cu_seqlens, const float *s0,
+                                    const Geometry &geo, void *ws, hipStream_t stream);
+hipError_t launch_state_grad_bf16(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0,
+                                  const Geometry &geo, void *ws, hipStream_t stream);
+hipError_t launch_grad_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *d_out, const int32_t *cu_seqlens, void *dq, void *dk, void *dv, float *dg,
+                            float *dbeta, const Geometry &geo, const void *ws, hipStream_t stream);
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
                              const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                              const Geometry &geo, const void *ws, hipStream_t stream);

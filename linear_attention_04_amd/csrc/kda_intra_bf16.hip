@@ -14,12 +14,13 @@ namespace {
 
 constexpr int kWaves = 4;
 
-template <bool SCALAR_GATE>
+// BWD: also each chunk's backward record, to `brecords` ([H][max_chunks] like the records).
+template <bool SCALAR_GATE, bool BWD>
 __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ chunk_seq, int64_t T, int H, int N, int64_t max_chunks,
-    char *__restrict__ records) {
+    char *__restrict__ records, char *__restrict__ brecords) {
     __shared__ intra::IntraLds lds[kWaves];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
@@ -37,14 +38,13 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     chunk_span(cu, chunk_off, chunk_seq, chunk, T, N, max_chunks, start, len);
     if (len == 0) return;  // same chunk for the whole workgroup
     char *rec = records + ((size_t)h * max_chunks + chunk) * kRecBytesBf16;  // head-major
-    intra::chunk_record<SCALAR_GATE>(q, k, g, beta, start, len, h, H, head_ok, lds[wave], rec, lane);
+    char *brec = BWD ? brecords + ((size_t)h * max_chunks + chunk) * kBRecBytes : nullptr;
+    intra::chunk_record<SCALAR_GATE, BWD>(q, k, g, beta, start, len, h, H, head_ok, lds[wave], rec, lane, brec);
 }
 
-}  // namespace
-
-hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const float *beta,
-                             const int32_t *cu_seqlens, const Geometry &geo, void *ws,
-                             hipStream_t stream) {
+template <bool BWD>
+hipError_t launch_intra(const void *q, const void *k, const float *g, const float *beta, const int32_t *cu_seqlens,
+                        const Geometry &geo, void *ws, hipStream_t stream) {
     if (geo.max_chunks == 0) return hipSuccess;
     char *base = static_cast<char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
@@ -52,12 +52,25 @@ hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const
     const int64_t blocks = geo.max_chunks * ((geo.H + kWaves - 1) / kWaves);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
-    auto kern = geo.scalar_gate ? kda_intra_bf16_kernel<true> : kda_intra_bf16_kernel<false>;
+    auto kern = geo.scalar_gate ? kda_intra_bf16_kernel<true, BWD> : kda_intra_bf16_kernel<false, BWD>;
     hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), 0, stream,
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), g, beta,
                        cu_seqlens, chunk_off, chunk_seq, geo.T, geo.H, geo.N, geo.max_chunks,
-                       base + geo.off_records);
+                       base + geo.off_records, BWD ? base + geo.off_brecords : nullptr);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const float *beta,
+                             const int32_t *cu_seqlens, const Geometry &geo, void *ws,
+                             hipStream_t stream) {
+    return launch_intra<false>(q, k, g, beta, cu_seqlens, geo, ws, stream);
+}
+
+hipError_t launch_intra_bf16_bwd(const void *q, const void *k, const float *g, const float *beta,
+                                 const int32_t *cu_seqlens, const Geometry &geo, void *ws, hipStream_t stream) {
+    return launch_intra<true>(q, k, g, beta, cu_seqlens, geo, ws, stream);
 }
 
 }  // namespace kda

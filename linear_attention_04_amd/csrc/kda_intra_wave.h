@@ -68,11 +68,13 @@ __device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
 // one decay per token and head for all channels (the scalar-gated delta rule); the
 // per-channel gate arithmetic then works on one value per lane, which the
 // compiler shares across the channels. Lane l holds token l % 16 of the chunk.
-template <bool SCALAR_GATE>
+// BWD: also the backward record (same factors in the operand layouts of the reverse
+// pass) to `brec` in global memory.
+template <bool SCALAR_GATE, bool BWD = false>
 __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                                              const float *__restrict__ g, const float *__restrict__ beta,
                                              int64_t start, int len, int h, int H, bool head_ok, IntraLds &L,
-                                             char *rec, int lane) {
+                                             char *rec, int lane, char *brec = nullptr) {
     const int c = lane & 15;
     const int grp = lane >> 4;
 
@@ -112,7 +114,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4];
+        unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4], kdr[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = 8 * s + 2 * u;
@@ -120,8 +122,16 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
             const float up0 = __expf(d0), up1 = __expf(d1);
             const float dn0 = __expf(-d0), dn1 = __expf(-d1);
             const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);  // channel of e; e + 1 is ch + 1
-            L.kd[ch * kChStride + c] = to_bf16(kr[e] * (dn0 * row_bcast<15>(up0)));
-            L.kd[(ch + 1) * kChStride + c] = to_bf16(kr[e + 1] * (dn1 * row_bcast<15>(up1)));
+            const __bf16 kd0 = to_bf16(kr[e] * (dn0 * row_bcast<15>(up0)));
+            const __bf16 kd1 = to_bf16(kr[e + 1] * (dn1 * row_bcast<15>(up1)));
+            L.kd[ch * kChStride + c] = kd0;
+            L.kd[(ch + 1) * kChStride + c] = kd1;
+            if (BWD) {
+                bf16x2 pr;
+                pr[0] = kd0;
+                pr[1] = kd1;
+                kdr[u] = __builtin_bit_cast(unsigned int, pr);  // elements 2u, 2u + 1 of slab s
+            }
             split_pair(kr[e] * up0, kr[e + 1] * up1, khh[u], khl[u]);
             split_pair(qr[e] * up0, qr[e + 1] * up1, qhh[u], qhl[u]);
             split_pair(kr[e] * dn0, kr[e + 1] * dn1, kbh[u], kbl[u]);
@@ -138,6 +148,9 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         acc_p = mfma_16x16x32(vqhh, vkbh, acc_p);
         acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
         acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
+        if (BWD && head_ok)  // K^d in the W layout: token c, channels 16j + 4grp + i
+            *reinterpret_cast<uint4 *>(brec + kBRecKD + (s * 64 + lane) * 16) =
+                make_uint4(kdr[0], kdr[1], kdr[2], kdr[3]);
     }
 
     wave_sync();
@@ -256,6 +269,33 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         // gamma_perm[grp][4c + i] = gamma[16c + 4grp + i]
         const float4 gv = *reinterpret_cast<const float4 *>(&L.gam[16 * c + 4 * grp]);
         *reinterpret_cast<float4 *>(rec + kRecGAM + (grp * 32 + 4 * c) * 4) = gv;
+        if (BWD) *reinterpret_cast<float4 *>(brec + kBRecGAM + (grp * 32 + 4 * c) * 4) = gv;
+    }
+    if (BWD) {
+        // W and Q~ channel-major through the K+ area (its last reads were above),
+        // then read back in the K^d layout: lane (c, grp), pair mp holds channel
+        // 32 mp + c (low 8 bytes) and 32 mp + 16 + c (high 8 bytes), tokens 4grp .. + 3
+        wave_sync();
+        __bf16 *tw = reinterpret_cast<__bf16 *>(L.kp);
+        __bf16 *tq = tw + KD * kChStride;
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 16 * jt + 4 * grp + i;
+                tw[ch * kChStride + c] = wv[jt >> 1][4 * (jt & 1) + i];
+                tq[ch * kChStride + c] = qv[jt >> 1][4 * (jt & 1) + i];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int mp = 0; mp < 4; ++mp) {
+            const int lo = (32 * mp + c) * kChStride + 4 * grp, hi = (32 * mp + 16 + c) * kChStride + 4 * grp;
+            const uint2 wl = *reinterpret_cast<const uint2 *>(&tw[lo]), wh = *reinterpret_cast<const uint2 *>(&tw[hi]);
+            const uint2 ql = *reinterpret_cast<const uint2 *>(&tq[lo]), qh = *reinterpret_cast<const uint2 *>(&tq[hi]);
+            *reinterpret_cast<uint4 *>(brec + kBRecWT + (mp * 64 + lane) * 16) = make_uint4(wl.x, wl.y, wh.x, wh.y);
+            *reinterpret_cast<uint4 *>(brec + kBRecQT + (mp * 64 + lane) * 16) = make_uint4(ql.x, ql.y, qh.x, qh.y);
+        }
     }
 }
 

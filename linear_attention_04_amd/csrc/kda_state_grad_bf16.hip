@@ -1,0 +1,302 @@
+// kda_state_grad_bf16.hip -- reverse recurrent kernel of the backward pass, bf16 io,
+// K = V = 128.
+//
+// Over one sequence, with R the gradient reaching a chunk's end state, each chunk
+// (taken last to first) maps R to the gradient reaching its start state:
+//     X = K^d R,   R <- Diag(gamma) R + Q~^T dO - W^T X,
+// the transpose of the forward's state map S_C = Diag(gamma) S_0 + K^d^T (T' V - W S_0)
+// plus the output's Q~ S_0 term (W, Q~, K^d, gamma as in the intra-chunk kernel). R
+// at each chunk end is stored for the token-parallel gradient kernel (bf16 fragments,
+// the layout the forward recomputation stores the start states in), and R after the
+// first chunk is the initial state's gradient.
+//
+// The workgroup mirrors the forward recurrent kernel: 32 value columns of one
+// (sequence, head) as two 16-column tiles, each tile's 128 x 16 slice of R held in MFMA
+// accumulators by two waves (64 key rows each), two producer waves streaming each
+// chunk's backward record and d_out tile into an LDS ring with direct buffer->LDS
+// loads, one barrier per chunk. X is a sum over all 128 keys, so the two halves of a
+// tile swap their partial X through LDS at the barrier and both form the same sum.
+#include "kda_chunks.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_ring.h"
+
+namespace kda {
+namespace {
+
+constexpr int KD = 128;
+constexpr int VD = 128;
+constexpr int kTiles = VD / 16;
+
+// Ring slot (16 KiB): backward record bytes [0, 12288) as 12 wave-wide 1 KiB loads,
+// gamma (512 B) loaded twice into [12288, 13312), the d_out tile [16 tokens][32
+// columns] bf16 at kDOff. Producer p issues record pieces 6p .. 6p + 5, then gamma
+// (p = 0) or the d_out tile (p = 1): kPerWave loads per chunk each.
+constexpr int kNW = 2;
+constexpr int kPerWave = 7;
+constexpr int kSlotBytes = 16384;
+constexpr int kGamOff = kBRecGAM;
+constexpr int kDOff = kBRecGAM + 1024;
+static_assert(kBRecGAM == 12288 && kBRecBytes == 12800 && kDOff + 1024 <= kSlotBytes, "backward record layout");
+
+constexpr int kHalves = 2;
+constexpr int kComputeWaves = kNW * kHalves;
+constexpr int kWaves = kComputeWaves + kNW;
+
+// Exchange area after the ring: [chunk parity][tile][half][64 lanes] f32x4, each half's
+// partial X.
+constexpr int kXchgBytes = 2 * kNW * kHalves * 1024;
+
+struct LaneOffsets {
+    unsigned int rec;   // lane * 16
+    unsigned int gam;   // (lane & 31) * 16
+    unsigned int d;     // d_out tile load of this lane: token row lane / 4, 8 columns
+    unsigned int vrow;  // one token row of d_out in bytes (H * VD * 2)
+};
+
+__device__ __forceinline__ int tile_bytes(int len, unsigned int vrow) {
+    return len > 0 ? (len - 1) * (int)vrow + kNW * 32 : 0;
+}
+
+__device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const char *brec, const char *dchunk,
+                                            int len, int producer, const LaneOffsets &lo) {
+    const __amdgpu_buffer_rsrc_t rr = rsrc(brec, kBRecBytes);
+#pragma unroll
+    for (int k = 0; k < kPerWave - 1; ++k) {
+        const int piece = (kPerWave - 1) * producer + k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + piece * 1024), 16, lo.rec,
+                                                 piece * 1024, 0, 0);
+    }
+    if (producer == 0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + kGamOff), 16, lo.gam, kBRecGAM, 0,
+                                                 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dchunk, tile_bytes(len, lo.vrow));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(ring + slot + kDOff), 16, lo.d, 0, 0, 0);
+    }
+}
+
+// One chunk's operands for one half (rows 64 KH .. 64 KH + 63 of a tile).
+struct HalfOps {
+    bf16x8 kd[2];  // K^d slabs 2 KH, 2 KH + 1 (token c, keys 32s + 4grp + i, 32s + 16 + 4grp + i)
+    bf16x8 wt[4];  // W^T tiles 4 KH .. + 3, tokens 4grp .. + 3 twice (both halves of the reduction)
+    s16x4 qt[4];   // Q~^T tiles 4 KH .. + 3, tokens 4grp .. + 3
+    float2 gam;
+    s16x4 dd;      // d_out: tokens 4grp .. + 3 of column c
+};
+
+template <int KH>
+__device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, int lane) {
+    const int c = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        o.kd[s] = *reinterpret_cast<const bf16x8 *>(slot + kBRecKD + ((2 * KH + s) * 64 + lane) * 16);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+        const int m = 4 * KH + mm;
+        const int base = ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8;
+        int off = kBRecWT + base;
+        const uint2 a = *reinterpret_cast<const uint2 *>(slot + off);
+        asm volatile("" : "+v"(off));  // a second read of the same bytes, not a register copy
+        const uint2 b = *reinterpret_cast<const uint2 *>(slot + off);
+        o.wt[mm] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+        o.qt[mm] = *reinterpret_cast<const s16x4 *>(slot + kBRecQT + base);
+    }
+    o.gam = *reinterpret_cast<const float2 *>(slot + kGamOff + (grp * 32 + 2 * c) * 4);
+    // rows past the end of a short chunk were loaded as zeros (range-checked loads)
+    const unsigned short *d16 = reinterpret_cast<const unsigned short *>(slot + kDOff);
+    s16x4 dd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dd[i] = (short)d16[(4 * grp + i) * (kNW * 16) + vt * 16 + c];
+    o.dd = dd;
+}
+
+// Before the barrier: R (the gradient at the chunk end) to the store, this half's
+// partial X = K^d R over its 64 keys to the partner, then Diag(gamma) R + Q~^T dO.
+template <int KH>
+__device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&R)[4], f32x4 &x, char *xchg, int lane,
+                                             char *rdst) {
+    bf16x8 rb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rb[s][i] = to_bf16(R[2 * s][i]);
+            rb[s][4 + i] = to_bf16(R[2 * s + 1][i]);
+        }
+    }
+    *reinterpret_cast<bf16x8 *>(rdst) = rb[0];
+    *reinterpret_cast<bf16x8 *>(rdst + 1024) = rb[1];
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    x = mfma_16x16x32(o.kd[0], rb[0], zero);
+    x = mfma_16x16x32(o.kd[1], rb[1], x);
+    *reinterpret_cast<f32x4 *>(xchg + KH * 1024 + lane * 16) = x;
+    decay_tile<4 * KH + 0>(R[0], o.gam);
+    decay_tile<4 * KH + 1>(R[1], o.gam);
+    decay_tile<4 * KH + 2>(R[2], o.gam);
+    decay_tile<4 * KH + 3>(R[3], o.gam);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) R[mm] = mfma_16x16x16(o.qt[mm], o.dd, R[mm]);
+}
+
+// After the barrier: X from both halves (half 0's part first on both, so they hold
+// bitwise equal X), then R -= W^T X with X split into two bf16 terms.
+template <int KH>
+__device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&R)[4], const f32x4 &x, const f32x4 &px) {
+    const f32x4 x0 = KH == 0 ? x : px;
+    const f32x4 x1 = KH == 0 ? px : x;
+    const f32x4 d = -(x0 + x1);
+    bf16x8 db;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        db[i] = to_bf16(d[i]);
+        db[4 + i] = to_bf16(d[i] - from_bf16(db[i]));
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) R[mm] = mfma_16x16x32(o.wt[mm], db, R[mm]);
+}
+
+// The chunk loop of compute wave (vt, KH): barrier B_j (j = 0 .. nchunks) as in the
+// forward recurrent kernel, with the chunks taken last to first (step j works on
+// chunk nchunks - 1 - j). rdst0 points at this lane's fragment of the sequence's first
+// chunk in the end-state gradient array.
+template <int KH, int DEPTH>
+__device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t nchunks, int vt, int lane,
+                                             char *rdst0) {
+    auto slot_of = [&](int64_t j) {
+        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+    };
+    auto xchg_of = [&](int64_t j) { return ring + DEPTH * kSlotBytes + ((int)(j & 1) * kNW + vt) * kHalves * 1024; };
+    auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
+        f32x4 x, px;
+        char *xc = xchg_of(j);
+        chunk_part_a<KH>(cur, R, x, xc, lane, rdst0 + (size_t)(nchunks - 1 - j) * kStateBytesBf16);
+        wait_lgkm0();  // the partial X is in LDS before the barrier
+        barrier();     // B_{j+1}
+        px = *reinterpret_cast<const f32x4 *>(xc + (1 - KH) * 1024 + lane * 16);
+        read_ops<KH>(next, slot_of(j + 1), vt, lane);
+        chunk_part_b<KH>(cur, R, x, px);
+    };
+    HalfOps opa, opb;
+    barrier();  // B_0
+    read_ops<KH>(opa, slot_of(0), vt, lane);
+    int64_t j = 0;
+    for (; j + 2 <= nchunks; j += 2) {
+        step(j, opa, opb);
+        step(j + 1, opb, opa);
+    }
+    if (j < nchunks) step(j, opa, opb);
+}
+
+template <int DEPTH>
+__global__ __launch_bounds__(64 * kWaves) void kda_state_grad_bf16_kernel(
+    const unsigned short *__restrict__ d_out, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+    const float *__restrict__ dsT, float *__restrict__ ds0, int64_t T, int H, int N, int64_t max_chunks,
+    const char *__restrict__ brecords, char *__restrict__ dstates) {
+    static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
+    static_assert((DEPTH - 1) * kPerWave < 64, "a producer's loads in flight must fit the 6-bit counter");
+    extern __shared__ __attribute__((aligned(1024))) char ring[];
+    int pair, vg;
+    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    if (pair >= N * H) return;  // whole workgroup
+    const int n = pair / H, h = pair % H;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int col0 = vg * kNW * 16;
+    const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
+    const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
+    const size_t head_chunk0 = (size_t)h * max_chunks + sc.chunk_begin;  // [H][max_chunks] index of chunk 0
+
+    if (wid >= kComputeWaves) {
+        // ---- producer: chunk nchunks - 1 - j into slot j % DEPTH ----
+        const int p = wid - kComputeWaves;
+        LaneOffsets lo;
+        lo.vrow = (unsigned int)H * VD * 2;
+        lo.rec = lane * 16;
+        lo.gam = (lane & 31) * 16;
+        lo.d = (lane >> 2) * lo.vrow + (lane & 3) * 16;
+        const char *rec0 = brecords + head_chunk0 * kBRecBytes;
+        const char *d0 = reinterpret_cast<const char *>(d_out) + ((size_t)sc.tok_begin * H + h) * VD * 2 +
+                         (size_t)col0 * 2;
+        const size_t chunk_rows = (size_t)16 * lo.vrow;
+        auto issue = [&](int64_t j) {
+            const int64_t c = nchunks - 1 - j;
+            const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * c);
+            const int len = rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
+            const unsigned int slot = (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+            issue_chunk(ring, slot, rec0 + (size_t)c * kBRecBytes, d0 + (size_t)c * chunk_rows, len, p, lo);
+        };
+        for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
+        for (int64_t j = 0; j < nchunks; ++j) {
+            const int64_t lim = j == 0 ? DEPTH - 2 : j + DEPTH - 3;
+            const int64_t last = lim < nchunks - 1 ? lim : nchunks - 1;
+            asm volatile("" ::: "memory");
+            wait_for_chunk<kPerWave, DEPTH>((int)(last - j));
+            barrier();  // B_j
+            // the slot of step j - 2 is free (read after B_{j-2}, consumed before B_{j-1})
+            if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
+        }
+        barrier();  // B_nchunks
+        return;
+    }
+
+    // ---- compute wave (vt, kh): value columns col0 + 16 vt .. + 15, key rows 64 kh .. + 63 ----
+    const int c = lane & 15, grp = lane >> 4;
+    const int vt = wid >> 1, kh = wid & 1;
+    f32x4 R[4];
+    const size_t sbase = (size_t)pair * KD * VD + (size_t)(64 * kh) * VD + col0 + vt * 16 + c;
+    if (dsT) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R[m][i] = dsT[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) R[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    wait_vmcnt<0>();  // settle the loads before the loop (stores share the counter)
+    char *rdst0 = dstates + head_chunk0 * kStateBytesBf16 +
+                  ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16;
+    if (kh == 0)
+        compute_wave<0, DEPTH>(R, ring, nchunks, vt, lane, rdst0);
+    else
+        compute_wave<1, DEPTH>(R, ring, nchunks, vt, lane, rdst0);
+    if (ds0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds0[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = R[m][i];
+    }
+}
+
+template <int DEPTH>
+hipError_t launch(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0, const Geometry &geo,
+                  void *ws, hipStream_t stream) {
+    const int pairs = geo.N * geo.H;
+    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / kNW);
+    char *base = static_cast<char *>(ws);
+    const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
+    const size_t lds = (size_t)DEPTH * kSlotBytes + kXchgBytes;
+    auto kern = kda_state_grad_bf16_kernel<DEPTH>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kWaves), lds, stream, static_cast<const unsigned short *>(d_out),
+                       cu_seqlens, chunk_off, dsT, ds0, geo.T, geo.H, geo.N, geo.max_chunks,
+                       base + geo.off_brecords, base + geo.off_dstates);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_grad_bf16(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0,
+                                  const Geometry &geo, void *ws, hipStream_t stream) {
+    // as the forward recurrent kernel: an 8-deep ring with at most one workgroup per
+    // CU, else 4 deep so that two fit
+    constexpr int kCUs = 256;
+    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
+    if (blocks <= kCUs) return launch<8>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
+    return launch<4>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
+}
+
+}  // namespace kda

@@ -21,6 +21,9 @@ mix, so every input here is synthetic:
 * For bf16 workloads q, k and v are rounded to bf16 (round to nearest even);
   g, beta and the states stay fp32.
 * Initial states, where a workload has one, are 0.02 * N(0, 1) in fp32.
+* Backward passes receive d_out ~ N(0, 1) (bf16-exact for bf16 workloads) and a
+  final-state gradient 0.02 * N(0, 1) in fp32, from a stream of their own
+  (:func:`output_gradients`).
 
 Random numbers are drawn block by block over 1024-token blocks with
 ``numpy.random.default_rng([seed, block])`` in the order q, k, v, beta, g, so a
@@ -37,6 +40,7 @@ import numpy as np
 BLOCK_TOKENS = 1024
 _STATE_STREAM = 10**6
 _LENGTH_STREAM = 10**6 + 1
+_GRAD_STREAM = 10**6 + 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -168,6 +172,18 @@ def initial_state(w: Workload) -> np.ndarray | None:
     rng = np.random.default_rng([w.seed, _STATE_STREAM])
     s = rng.standard_normal((w.num_seqs, w.heads, w.head_k, w.head_v), dtype=np.float32)
     return (np.float32(0.02) * s).astype(np.float32)
+
+
+def output_gradients(w: Workload) -> tuple:
+    """(d_out [T, H, V], d_final_state [N, H, K, V]) fp32, the gradients a backward pass
+    of ``w`` receives; d_out holds bf16-exact values for bf16 workloads."""
+    rng = np.random.default_rng([w.seed, _GRAD_STREAM])
+    T, H, K, V = w.total_tokens, w.heads, w.head_k, w.head_v
+    d_out = rng.standard_normal((T, H, V), dtype=np.float32)
+    if w.bf16:
+        d_out = round_to_bf16(d_out)
+    d_fs = (np.float32(0.02) * rng.standard_normal((w.num_seqs, H, K, V), dtype=np.float32)).astype(np.float32)
+    return d_out, d_fs
 
 
 def generate(w: Workload, threads: int | None = None) -> dict:

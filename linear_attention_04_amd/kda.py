@@ -32,6 +32,8 @@ EXPORTS = (
     "kda_intra_chunk",
     "kda_inter_chunk",
     "kda_decode_step",
+    "kda_backward_workspace_bytes",
+    "kda_chunk_prefill_backward",
     "kda_status_string",
     "kda_version",
 )
@@ -80,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_inter_chunk.restype = i32
     lib.kda_decode_step.argtypes = [p, p, p, p, p, p, p, dims_p, p]
     lib.kda_decode_step.restype = i32
+    lib.kda_backward_workspace_bytes.argtypes = [dims_p]
+    lib.kda_backward_workspace_bytes.restype = sz
+    lib.kda_chunk_prefill_backward.argtypes = [p] * 15 + [dims_p, p, sz, p]
+    lib.kda_chunk_prefill_backward.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -120,6 +126,19 @@ def kda_inter_chunk(v, cu_seqlens, initial_state, out, final_state, dims: KdaDim
 
 def kda_decode_step(q, k, v, g, beta, state, out, dims: KdaDims, stream) -> int:
     return int(load_library().kda_decode_step(q, k, v, g, beta, state, out, ctypes.byref(dims), stream))
+
+
+def kda_backward_workspace_bytes(dims: KdaDims) -> int:
+    return int(load_library().kda_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def kda_chunk_prefill_backward(q, k, v, g, beta, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,
+                               dg, dbeta, d_initial_state, dims: KdaDims, workspace, workspace_bytes: int,
+                               stream) -> int:
+    return int(load_library().kda_chunk_prefill_backward(q, k, v, g, beta, cu_seqlens, initial_state, d_out,
+                                                         d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                                                         ctypes.byref(dims), workspace, workspace_bytes,
+                                                         stream))
 
 
 def kda_status_string(status: int) -> str:
@@ -241,4 +260,45 @@ def decode_step(q, k, v, g, beta, state, out=None, stream=None):
     st = kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out), dims, s)
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
+    return out
+
+
+def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_state=None, d_final_state=None,
+                           want_d_initial_state=True, workspace=None, stream=None):
+    """Gradients of chunk_prefill (bf16, K = V = 128) for L = <d_out, out> +
+    <d_final_state, final_state>.
+
+    Inputs as :func:`chunk_prefill`, plus d_out [T, H, V] bf16 and d_final_state
+    [N, H, K, V] fp32 or None. Returns a dict: dq, dk [T, H, K] and dv [T, H, V] bf16,
+    dg fp32 shaped like g, dbeta [T, H] fp32, d_initial_state [N, H, K, V] fp32 (or
+    None when want_d_initial_state is False).
+    """
+    import torch
+
+    _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
+    if d_out.dtype != v.dtype or d_out.shape != v.shape or not d_out.is_cuda or not d_out.is_contiguous():
+        raise ValueError("d_out must be a contiguous device tensor like v")
+    dims = make_dims(q, v, cu_seqlens, g)
+    if d_final_state is not None:
+        want = (dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v)
+        if d_final_state.dtype != torch.float32 or tuple(d_final_state.shape) != want \
+                or not d_final_state.is_cuda or not d_final_state.is_contiguous():
+            raise ValueError("d_final_state must be a contiguous fp32 device tensor [N, H, K, V]")
+    if workspace is None:
+        nbytes = kda_backward_workspace_bytes(dims)
+        if nbytes == 0:
+            raise KdaError(KDA_ERR_UNSUPPORTED, "kda_backward_workspace_bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+               d_initial_state=torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
+                                           dtype=torch.float32, device=q.device)
+               if want_d_initial_state else None)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    st = kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                    _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(out["dq"]),
+                                    _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                    _ptr(out["d_initial_state"]), dims, _ptr(workspace), workspace.numel(), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_prefill_backward")
     return out

@@ -99,11 +99,13 @@ def chunked(q, k, v, g, beta, S0=None, chunk=16, ref=None, intermediates=False):
     return o, S
 
 
-def chunked_backward(q, k, v, g, beta, dO, S0=None, dST=None, chunk=16, ref=None):
+def chunked_backward(q, k, v, g, beta, dO, S0=None, dST=None, chunk=16, ref=None, intermediates=False):
     """Gradients of L = <dO, o> + <dS_T, S_T> through the chunked form above.
 
     One sequence of one head (shapes as :func:`chunked`, dO [T, V], dST [K, V]).
-    Returns dict(dq, dk, dv, dg, dbeta, dS0). The reverse pass runs over chunks;
+    Returns dict(dq, dk, dv, dg, dbeta, dS0), plus with ``intermediates`` the lists
+    S0s (each chunk's start state) and Rs (the gradient reaching each chunk's end
+    state), in chunk order. The reverse pass runs over chunks;
     R is the gradient reaching the chunk's end state. With the chunk's start
     state S0 and U = V - K+ S0, Delta = T diag(beta) U:
         dDelta = P^T dO + K^d R,      dU = (T diag(beta))^T dDelta,    dv = dU,
@@ -128,7 +130,9 @@ def chunked_backward(q, k, v, g, beta, dO, S0=None, dST=None, chunk=16, ref=None
     R = np.zeros((K, V)) if dST is None else _f64(dST).copy()
     dq, dk, dg = np.zeros((T, K)), np.zeros((T, K)), np.zeros((T, K))
     dv, dbeta = np.zeros((T, V)), np.zeros(T)
+    ends = [None] * len(starts)
     for ci in range(len(starts) - 1, -1, -1):
+        ends[ci] = R.copy()
         c0 = ci * chunk
         c1 = min(c0 + chunk, T)
         n = c1 - c0
@@ -174,4 +178,7 @@ def chunked_backward(q, k, v, g, beta, dO, S0=None, dST=None, chunk=16, ref=None
         dg[c0:c1] = np.cumsum(dG[::-1], axis=0)[::-1]
         dq[c0:c1], dk[c0:c1], dbeta[c0:c1] = dqc, dkc, dbeta_c
         R = gamma[:, None] * R + Qp.T @ D - Kp.T @ dU
-    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dS0=R)
+    res = dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dS0=R)
+    if intermediates:
+        res["S0s"], res["Rs"] = starts, ends
+    return res

@@ -140,3 +140,93 @@ def generate_on_device(w, keep_heads, threads: int = 16):
     host["initial_state"] = None if s0 is None else np.ascontiguousarray(s0[:, keep])
     host["cu_seqlens"] = cu
     return dev, host
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+
+# Tolerances per gradient tensor (bf16 io). Relative to the tensor: rel-L2 over the
+# whole tensor, and max|err| against the tensor's largest magnitude. See the design doc
+# for the derivation from the forward's bar.
+BWD_REL_L2 = 1e-2
+BWD_MAX_REL = 2e-2
+
+_ALIGN = 256
+_REC_BYTES = 14848
+_BREC_BYTES = 12800
+_STATE_BYTES = 32768
+
+
+def _align(x):
+    return (x + _ALIGN - 1) // _ALIGN * _ALIGN
+
+
+def backward_workspace_layout(T, H, N):
+    """Byte offsets of the backward workspace areas (bf16, K = V = 128), as the
+    library lays them out; tests check the total against kda_backward_workspace_bytes."""
+    max_chunks = (T + 15 * N) // 16
+    per = max_chunks * H
+    off_chunk_seq = _align(4 * (N + 1))
+    off_records = off_chunk_seq + _align(4 * max_chunks)
+    total = off_records + per * _REC_BYTES
+    off_brecords = _align(total)
+    off_states = _align(off_brecords + per * _BREC_BYTES)
+    off_dstates = _align(off_states + per * _STATE_BYTES)
+    return dict(max_chunks=max_chunks, off_states=off_states, off_dstates=off_dstates,
+                total=off_dstates + per * _STATE_BYTES)
+
+
+def decode_state_fragments(raw: np.ndarray) -> np.ndarray:
+    """A 128 x 128 bf16 state in fragment layout (32768 bytes) -> [key][value] fp64:
+    fragment (ct, ks), lane (c, grp), element e holds value column 16 ct + c and key
+    32 ks + 4 grp + e (e < 4) or 32 ks + 16 + 4 grp + e - 4."""
+    u16 = np.frombuffer(np.ascontiguousarray(raw).tobytes(), dtype=np.uint16).reshape(8, 4, 64, 8)
+    vals = (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = np.empty((128, 128))
+    lane = np.arange(64)
+    c, grp = lane % 16, lane // 16
+    for ct in range(8):
+        for ks in range(4):
+            for e in range(8):
+                key = 32 * ks + (4 * grp + e if e < 4 else 16 + 4 * grp + e - 4)
+                out[key, 16 * ct + c] = vals[ct, ks, :, e]
+    return out
+
+
+def upload_backward(x: dict, d_out, d_fs, packed: bool):
+    d = upload(x, True, packed)
+    d["d_out"] = to_device(d_out, True)
+    d["d_final_state"] = to_device(d_fs, False)
+    return d
+
+
+def run_gpu_backward(d: dict, want_d_initial_state=True, workspace=None):
+    from linear_attention_04_amd import kda
+
+    torch = torch_mod()
+    r = kda.chunk_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_out"],
+                                   cu_seqlens=d["cu_seqlens"], initial_state=d["initial_state"],
+                                   d_final_state=d["d_final_state"],
+                                   want_d_initial_state=want_d_initial_state, workspace=workspace)
+    torch.cuda.synchronize()
+    return r
+
+
+def run_oracle_backward(x: dict, d_out, d_fs, packed: bool, heads=None):
+    return oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_out,
+                           cu_seqlens=x["cu_seqlens"] if packed else None,
+                           initial_state=x.get("initial_state"), d_final_state=d_fs, heads=heads)
+
+
+def assert_close_rel(name, got, ref, rel_l2=None, max_rel=None):
+    rel_l2 = BWD_REL_L2 if rel_l2 is None else rel_l2
+    max_rel = BWD_MAX_REL if max_rel is None else max_rel
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    max_abs, rel = errors(got, ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    print(f"  {name}: max|err|={max_abs:.3e} (max|ref|={scale:.3e}) relL2={rel:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert rel <= rel_l2, f"{name}: rel-L2 {rel:.3e} > {rel_l2}"
+    assert max_abs <= max_rel * max(scale, 1e-30), f"{name}: max|err| {max_abs:.3e} > {max_rel} * {scale:.3e}"
+    return max_abs, rel

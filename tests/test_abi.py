@@ -118,3 +118,37 @@ def test_decode_argument_checks(lib):
     assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=2), None) == kda.KDA_ERR_ARG
     assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=4, K=64, V=64), None) == kda.KDA_ERR_UNSUPPORTED
     assert kda.kda_decode_step(p, p, p, p, p, p, p, dims(T=4, N=4, gate=3), None) == kda.KDA_ERR_ARG
+
+
+def test_backward_workspace_bytes(lib):
+    from tests import gpu_util as gu
+
+    for T, H, N in ((64, 2, 1), (8192, 64, 1), (300, 5, 7), (0, 3, 2)):
+        d = dims(T=T, H=H, N=N)
+        assert kda.kda_backward_workspace_bytes(d) == gu.backward_workspace_layout(T, H, N)["total"]
+        assert kda.kda_backward_workspace_bytes(d) > kda.kda_workspace_bytes(d)
+    # bf16 only; invalid sizes give 0
+    assert kda.kda_backward_workspace_bytes(dims(io=kda.KDA_IO_F32, K=16, V=16)) == 0
+    assert kda.kda_backward_workspace_bytes(dims(K=64, V=64)) == 0
+    assert kda.kda_backward_workspace_bytes(dims(H=0)) == 0
+
+
+def test_backward_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    d = dims()
+    need = kda.kda_backward_workspace_bytes(d)
+    ok = [p] * 5 + [None, None, p, None] + [p] * 5 + [None]
+    assert kda.kda_chunk_prefill_backward(*ok, d, p, need - 1, None) == kda.KDA_ERR_WORKSPACE
+    bad = list(ok)
+    bad[7] = None  # d_out
+    assert kda.kda_chunk_prefill_backward(*bad, d, p, need, None) == kda.KDA_ERR_ARG
+    bad = list(ok)
+    bad[10] = b.at(4)  # dk misaligned
+    assert kda.kda_chunk_prefill_backward(*bad, d, p, need, None) == kda.KDA_ERR_ALIGN
+    bad = list(ok)
+    bad[14] = b.at(8)  # d_initial_state misaligned
+    assert kda.kda_chunk_prefill_backward(*bad, d, p, need, None) == kda.KDA_ERR_ALIGN
+    assert kda.kda_chunk_prefill_backward(*ok, dims(N=2), p, 1 << 40, None) == kda.KDA_ERR_ARG
+    assert kda.kda_chunk_prefill_backward(*ok, dims(io=kda.KDA_IO_F32, K=16, V=16), p, 1 << 40, None) == \
+        kda.KDA_ERR_UNSUPPORTED

@@ -1,0 +1,123 @@
+"""GPU parity of the backward pass (kda_chunk_prefill_backward through the C ABI)
+against the fp64 oracle's reverse-mode gradients, at sizes the oracle finishes in
+seconds: several chunks and heads, ragged tails, packed sequences with empty ones,
+both gate kinds, with and without initial states and final-state gradients."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_04_amd import inputs
+from oracle import reference
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_04_amd import kda
+
+    kda.load_library()  # fails loudly when the HIP library is missing
+
+
+def _case(name, seed, H, T=None, state=True, gate=0.1, lengths=None, gate_kind="channel"):
+    w = inputs.custom_workload(name, seed, heads=H, total_tokens=T, head_k=128, head_v=128, io_dtype="bf16",
+                               gate_scale=gate, has_initial_state=state, lengths=lengths, gate=gate_kind)
+    x = inputs.generate(w)
+    d_out, d_fs = inputs.output_gradients(w)
+    return w, x, d_out, d_fs
+
+
+def _check(w, x, d_out, d_fs, packed, use_dfs=True):
+    print(f"case {w.name}: H={w.heads} T={w.total_tokens} N={w.num_seqs} gate={w.gate} "
+          f"state={w.has_initial_state} dfs={use_dfs}", flush=True)
+    d_fs = d_fs if use_dfs else None
+    d = gu.upload_backward(x, d_out, d_fs, packed)
+    got = gu.run_gpu_backward(d)
+    ref = gu.run_oracle_backward(x, d_out, d_fs, packed)
+    for name in GRADS:
+        gu.assert_close_rel(name, gu.to_host(got[name]), ref[name])
+    gu.assert_close_rel("d_initial_state", gu.to_host(got["d_initial_state"]), ref["d_initial_state"])
+    return d, got, ref
+
+
+def test_backward_small_with_intermediates():
+    """One sequence, two heads, four chunks; also the workspace's chunk start states
+    and end-state gradients against the chunked reference."""
+    torch = gu.torch_mod()
+    w, x, d_out, d_fs = _case("bwd_small", 101, H=2, T=64)
+    d = gu.upload_backward(x, d_out, d_fs, False)
+    lay = gu.backward_workspace_layout(w.total_tokens, w.heads, 1)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    got = gu.run_gpu_backward(d, workspace=ws)
+    raw = ws.cpu().numpy()
+    for h in range(w.heads):
+        r = reference.chunked_backward(x["q"][:, h], x["k"][:, h], x["v"][:, h], x["g"][:, h], x["beta"][:, h],
+                                       d_out[:, h], x["initial_state"][0, h], d_fs[0, h], intermediates=True)
+        for ci in range(4):
+            o = (h * lay["max_chunks"] + ci) * 32768
+            s0 = gu.decode_state_fragments(raw[lay["off_states"] + o:lay["off_states"] + o + 32768])
+            rr = gu.decode_state_fragments(raw[lay["off_dstates"] + o:lay["off_dstates"] + o + 32768])
+            gu.assert_close_rel(f"S0[h{h},c{ci}]", s0, r["S0s"][ci])
+            gu.assert_close_rel(f"R[h{h},c{ci}]", rr, r["Rs"][ci])
+    ref = gu.run_oracle_backward(x, d_out, d_fs, False)
+    for name in GRADS:
+        gu.assert_close_rel(name, gu.to_host(got[name]), ref[name])
+    gu.assert_close_rel("d_initial_state", gu.to_host(got["d_initial_state"]), ref["d_initial_state"])
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100, 333])
+def test_backward_lengths(T):
+    w, x, d_out, d_fs = _case(f"bwd_t{T}", 110 + T, H=5, T=T)
+    _check(w, x, d_out, d_fs, False)
+
+
+def test_backward_packed_ragged():
+    w, x, d_out, d_fs = _case("bwd_packed", 120, H=4, lengths=[1, 15, 16, 17, 47, 0, 64, 100, 3])
+    _check(w, x, d_out, d_fs, True)
+
+
+def test_backward_scalar_gate():
+    w, x, d_out, d_fs = _case("bwd_scalar", 121, H=3, T=150, gate_kind="scalar")
+    _check(w, x, d_out, d_fs, False)
+
+
+def test_backward_scalar_gate_packed():
+    w, x, d_out, d_fs = _case("bwd_scalar_packed", 122, H=2, lengths=[40, 0, 77, 16], gate_kind="scalar")
+    _check(w, x, d_out, d_fs, True)
+
+
+def test_backward_no_state_no_final_gradient():
+    w, x, d_out, d_fs = _case("bwd_nostate", 123, H=2, T=90, state=False)
+    d, got, ref = _check(w, x, d_out, d_fs, False, use_dfs=False)
+    # without them the optional output can be skipped, leaving the rest unchanged
+    got2 = gu.run_gpu_backward(d, want_d_initial_state=False)
+    assert got2["d_initial_state"] is None
+    for name in GRADS:
+        assert np.array_equal(gu.to_host(got2[name]), gu.to_host(got[name])), name
+
+
+def test_backward_long_memory_gate():
+    w, x, d_out, d_fs = _case("bwd_long_gate", 124, H=2, T=1000, gate=0.02)
+    _check(w, x, d_out, d_fs, False)
+
+
+def test_backward_all_sequences_empty():
+    """T = 0: the initial-state gradient is the final-state gradient."""
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+
+    H, N = 2, 3
+    d_fs = torch.randn((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    q = torch.empty((0, H, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, H, 128), dtype=torch.float32, device="cuda")
+    beta = torch.empty((0, H), dtype=torch.float32, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    r = kda.chunk_prefill_backward(q, q, q, g, beta, q, cu_seqlens=cu, d_final_state=d_fs)
+    torch.cuda.synchronize()
+    assert torch.equal(r["d_initial_state"], d_fs)
