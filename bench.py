@@ -36,6 +36,28 @@ INTRA_BYTES_PER_TH = {"channel": 1028 + 928, "scalar": 520 + 928}
 INTER_BYTES_PER_TH = 928 + 256 + 256
 STATE_BYTES = 128 * 128 * 4
 
+# Backward kernels, algorithmic bytes per (token, head):
+#  records:    q, k, g, beta in (1028; 520 scalar gate), forward + backward records
+#              out ((14848 + 12800) / 16 = 1728);
+#  states:     forward record (928) and v (256) in, every chunk's start state out
+#              (bf16, 32768 B / 16 tokens = 2048), plus the initial state if any;
+#  state_grad: backward record (800) and d_out (256) in, every chunk's end-state
+#              gradient out (2048), plus d_final_state in and d_initial_state out;
+#  token_grad: q, k, v, d_out (1024), g (512; 4 scalar), beta (4) and both stored
+#              states (4096) in; dq, dk, dv (768), dg (512; 4 scalar), dbeta (4) out.
+BWD_BYTES_PER_TH = {
+    "records": {"channel": 1028 + 1728, "scalar": 520 + 1728},
+    "states": {"channel": 928 + 256 + 2048, "scalar": 928 + 256 + 2048},
+    "state_grad": {"channel": 800 + 256 + 2048, "scalar": 800 + 256 + 2048},
+    "token_grad": {"channel": 1024 + 512 + 4 + 4096 + 768 + 512 + 4, "scalar": 1024 + 4 + 4 + 4096 + 768 + 4 + 4},
+}
+BWD_SOURCES = {
+    "records": ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_device.h", "kda_chunks.h"],
+    "states": ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
+    "state_grad": ["kda_state_grad_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
+    "token_grad": ["kda_grad_bf16.hip", "kda_device.h", "kda_chunks.h"],
+}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -47,8 +69,9 @@ def parse():
                     help="prefill workload (default: the H=64, T=8192 benchmark shape); see inputs.WORKLOADS")
     ap.add_argument("--gate", choices=("channel", "scalar"), default="channel",
                     help="scalar: the same shape with one gate per token and head (Gated DeltaNet)")
-    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
-                    help="decode: one-token state update of --decode-batch sequences x 64 heads")
+    ap.add_argument("--mode", choices=("prefill", "decode", "backward"), default="prefill",
+                    help="decode: one-token state update of --decode-batch sequences x 64 heads; "
+                         "backward: the gradients of the prefill (kda_chunk_prefill_backward, four stages)")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--fused", action="store_true",
                     help="time the single-kernel form (kda_chunk_prefill_fused) instead of the split")
@@ -194,6 +217,114 @@ def decode_bench(args):
     return 0
 
 
+def backward_bench(args, w, x):
+    """One step = one whole backward (its four stages) of workload ``w``."""
+    import numpy as np
+    import torch
+
+    from linear_attention_04_amd import inputs, kda
+
+    d_out_h, d_fs_h = inputs.output_gradients(w)
+    dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
+                         if bf else torch.from_numpy(a).to("cuda"))
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    g, beta = dev(x["g"], False), dev(x["beta"], False)
+    d_out, d_fs = dev(d_out_h, True), dev(d_fs_h, False)
+    T, H, N = w.total_tokens, w.heads, w.num_seqs
+    cu = torch.from_numpy(x["cu_seqlens"]).to("cuda") if N > 1 else None
+    s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).to("cuda")
+    cu_p = None if cu is None else cu.data_ptr()
+    s0_p = None if s0 is None else s0.data_ptr()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    ds0 = torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    dims = kda.make_dims(q, v, cu, g=g)
+    nbytes = kda.kda_backward_workspace_bytes(dims)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        st = [kda.kda_backward_records(P(q), P(k), P(g), P(beta), cu_p, dims, P(ws), nbytes, sp)]
+        rec(1)
+        st.append(kda.kda_backward_states(P(v), cu_p, s0_p, dims, P(ws), nbytes, sp))
+        rec(2)
+        st.append(kda.kda_backward_state_grad(P(d_out), cu_p, P(d_fs), P(ds0), dims, P(ws), nbytes, sp))
+        rec(3)
+        st.append(kda.kda_backward_token_grad(P(q), P(k), P(v), P(g), P(beta), P(d_out), cu_p, P(dq), P(dk),
+                                              P(dv), P(dg), P(dbeta), dims, P(ws), nbytes, sp))
+        rec(4)
+        bad = [e for e in st if e]
+        if bad:
+            raise kda.KdaError(bad[0], "backward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv, dg, dbeta)):
+        print("non-finite gradient", file=sys.stderr)
+        return 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("records", "states", "state_grad", "token_grad")
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    th = T * H
+    n_s0 = 1 if s0 is not None else 0
+    extra_states = {"records": 0, "states": n_s0, "state_grad": 2, "token_grad": 0}
+    kern_bytes = {n: BWD_BYTES_PER_TH[n][w.gate] * th + extra_states[n] * STATE_BYTES * N * H for n in names}
+    dom = max(names, key=lambda n: stage_ms[n])
+    achieved = kern_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    digest = source_digest(BWD_SOURCES[dom])
+    gate_bytes = 4 if w.gate == "scalar" else 512
+    compulsory = th * (4 * 256 + gate_bytes + 4 + 3 * 256 + gate_bytes + 4) + (n_s0 + 2) * STATE_BYTES * N * H
+    path_gbs = compulsory / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": (f"KDA prefill backward tokens/s (gradients of q, k, v, g, beta, initial state), "
+                   f"H={H} T={T} K=V=128 bf16" + (" (scalar gate)" if w.gate == "scalar" else "")),
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128, "num_seqs": N,
+                   "initial_state": s0 is not None, "chunk": 16, "gate": w.gate, "pass": "backward"},
+        "path_hbm": {"algorithmic_bytes": compulsory, "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": path_gbs / HBM_PEAK_GBS},
+        "kernels_ms": stage_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for("bwd_" + dom, digest, w.name),
+                     "algorithmic_bytes": kern_bytes[dom], "source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.max_threads()
+        heads = list(range(min(H, threads)))
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_out_h,
+                            cu_seqlens=x["cu_seqlens"] if N > 1 else None, initial_state=x["initial_state"],
+                            d_final_state=d_fs_h, heads=heads, threads=threads)
+            runs += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or runs >= 64:
+                break
+        rec["cpu_baseline"] = {
+            "value": runs * T * len(heads) / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {H} heads x {T} tokens run {runs} times in {dt:.2f} s, "
+                      f"scaled to all {H} heads"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -222,6 +353,8 @@ def main():
         print("bench.py times the bf16 path; the fp32 workload is a parity case", file=sys.stderr)
         return 2
     x = inputs.generate(w)
+    if args.mode == "backward":
+        return backward_bench(args, w, x)
     dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
                          if bf else torch.from_numpy(a).to("cuda"))
     q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)

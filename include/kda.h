@@ -182,6 +182,35 @@ int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, cons
                                void *stream);
 
 
+/* The four stages of kda_chunk_prefill_backward as separate calls, for callers that
+ * time or schedule them apart. Enqueued in this order on one stream with one
+ * workspace (of kda_backward_workspace_bytes) and the same dims and cu_seqlens, they
+ * do exactly what kda_chunk_prefill_backward does; arguments, layouts and status
+ * codes are that function's.
+ *   kda_backward_records: builds the chunk table and each chunk's factors (the
+ *       forward record and the backward record) from q, k, g, beta.
+ *   kda_backward_states: runs the forward recurrence again from initial_state
+ *       and stores every chunk's start state (no output).
+ *   kda_backward_state_grad: the reverse pass over the chunks from d_final_state,
+ *       storing every chunk's end-state gradient and writing d_initial_state (if
+ *       not NULL).
+ *   kda_backward_token_grad: dq, dk, dv, dg, dbeta from the stored states. */
+int kda_backward_records(const void *q, const void *k, const float *g, const float *beta,
+                         const int32_t *cu_seqlens, const kda_dims_t *dims, void *workspace,
+                         size_t workspace_bytes, void *stream);
+int kda_backward_states(const void *v, const int32_t *cu_seqlens, const float *initial_state,
+                        const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                        void *stream);
+int kda_backward_state_grad(const void *d_out, const int32_t *cu_seqlens,
+                            const float *d_final_state, float *d_initial_state,
+                            const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                            void *stream);
+int kda_backward_token_grad(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const void *d_out, const int32_t *cu_seqlens,
+                            void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                            const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);
 

@@ -207,44 +207,98 @@ size_t kda_backward_workspace_bytes(const kda_dims_t *dims) {
     return geo.backward_bytes;
 }
 
-int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                               const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
-                               const float *d_final_state, void *dq, void *dk, void *dv, float *dg, float *dbeta,
-                               float *d_initial_state, const kda_dims_t *dims, void *workspace,
-                               size_t workspace_bytes, void *stream) {
-    Geometry geo;
-    int st = kda::make_backward_geometry(dims, &geo);
+namespace {
+
+int check_backward(const kda_dims_t *dims, const int32_t *cu_seqlens, void *ws, size_t ws_bytes, Geometry *geo) {
+    const int st = kda::make_backward_geometry(dims, geo);
     if (st != KDA_OK) return st;
     if (cu_seqlens == nullptr && dims->num_seqs != 1) return KDA_ERR_ARG;
     if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < geo.backward_bytes) return KDA_ERR_WORKSPACE;
-    if (!kda::aligned16(workspace)) return KDA_ERR_ALIGN;
-    if (geo.T > 0) {
-        st = kda::check_pointers({q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta},
-                                 {initial_state, d_final_state, d_initial_state});
-    } else {
-        st = kda::check_pointers({}, {q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta, initial_state,
-                                      d_final_state, d_initial_state});
-    }
+    if (ws == nullptr || ws_bytes < geo->backward_bytes) return KDA_ERR_WORKSPACE;
+    if (!kda::aligned16(ws)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+// Pointers that must be set when there are tokens (all are optional when T = 0).
+int check_data(const Geometry &geo, std::initializer_list<const void *> required,
+               std::initializer_list<const void *> optional) {
+    if (geo.T > 0) return kda::check_pointers(required, optional);
+    int st = kda::check_pointers({}, required);
+    return st != KDA_OK ? st : kda::check_pointers({}, optional);
+}
+
+}  // namespace
+
+int kda_backward_records(const void *q, const void *k, const float *g, const float *beta,
+                         const int32_t *cu_seqlens, const kda_dims_t *dims, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK) st = check_data(geo, {q, k, g, beta}, {});
     if (st != KDA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (cu_seqlens != nullptr) {
         st = kda::launch_status(kda::launch_chunk_table(cu_seqlens, geo, workspace, s));
         if (st != KDA_OK) return st;
     }
-    if (geo.T > 0) {
-        // chunk factors in both layouts, then the forward again for every chunk's start state
-        st = kda::launch_status(kda::launch_intra_bf16_bwd(q, k, g, beta, cu_seqlens, geo, workspace, s));
-        if (st != KDA_OK) return st;
-        st = kda::launch_status(kda::launch_inter_bf16_states(v, cu_seqlens, initial_state, geo, workspace, s));
-        if (st != KDA_OK) return st;
-    }
-    // the reverse pass also carries d_final_state through empty sequences
-    st = kda::launch_status(
-        kda::launch_state_grad_bf16(d_out, cu_seqlens, d_final_state, d_initial_state, geo, workspace, s));
+    if (geo.T == 0) return KDA_OK;
+    return kda::launch_status(kda::launch_intra_bf16_bwd(q, k, g, beta, cu_seqlens, geo, workspace, s));
+}
+
+int kda_backward_states(const void *v, const int32_t *cu_seqlens, const float *initial_state,
+                        const kda_dims_t *dims, void *workspace, size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK) st = check_data(geo, {v}, {initial_state});
+    if (st != KDA_OK || geo.T == 0) return st;
+    return kda::launch_status(kda::launch_inter_bf16_states(v, cu_seqlens, initial_state, geo, workspace,
+                                                            static_cast<hipStream_t>(stream)));
+}
+
+int kda_backward_state_grad(const void *d_out, const int32_t *cu_seqlens, const float *d_final_state,
+                            float *d_initial_state, const kda_dims_t *dims, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK) st = check_data(geo, {d_out}, {d_final_state, d_initial_state});
+    if (st != KDA_OK) return st;
+    // also with T = 0: the final-state gradient passes through empty sequences
+    return kda::launch_status(kda::launch_state_grad_bf16(d_out, cu_seqlens, d_final_state, d_initial_state, geo,
+                                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
+int kda_backward_token_grad(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *d_out, const int32_t *cu_seqlens, void *dq, void *dk, void *dv, float *dg,
+                            float *dbeta, const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK) st = check_data(geo, {q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta}, {});
     if (st != KDA_OK || geo.T == 0) return st;
     return kda::launch_status(kda::launch_grad_bf16(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta,
-                                                    geo, workspace, s));
+                                                    geo, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                               const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                               const float *d_final_state, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                               float *d_initial_state, const kda_dims_t *dims, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK)
+        st = check_data(geo, {q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta},
+                        {initial_state, d_final_state, d_initial_state});
+    if (st != KDA_OK) return st;
+    st = kda_backward_records(q, k, g, beta, cu_seqlens, dims, workspace, workspace_bytes, stream);
+    if (st == KDA_OK) st = kda_backward_states(v, cu_seqlens, initial_state, dims, workspace, workspace_bytes, stream);
+    if (st == KDA_OK)
+        st = kda_backward_state_grad(d_out, cu_seqlens, d_final_state, d_initial_state, dims, workspace,
+                                     workspace_bytes, stream);
+    if (st == KDA_OK)
+        st = kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta, dims, workspace,
+                                     workspace_bytes, stream);
+    return st;
 }
 
 const char *kda_status_string(int status) {

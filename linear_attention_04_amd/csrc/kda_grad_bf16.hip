@@ -48,6 +48,8 @@ struct alignas(16) GradLds {
     float dat[256];  // dA~
     float dp[256];   // dP (i <= r)
     float beta[16];
+    bf16x8 delf[4][64];  // Delta, per 32-column slab: token c, the slab's columns (see below)
+    bf16x8 duf[4][64];   // dU, likewise
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -231,7 +233,6 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
 
     // ================= 2. products over the keys, per 32-column value slab =================
     f32x4 dpa = zero4(), dtpa = zero4();  // dP[4grp + i][c], dT'[4grp + i][c]
-    bf16x8 delf[4], duf[4];               // Delta and dU per slab (token c, slab's 8 columns)
 #pragma unroll 1
     for (int p = 0; p < 4; ++p) {
         f32x4 ksv[2], kst[2], xv[2], xt[2];
@@ -286,15 +287,15 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             if (row_ok) *reinterpret_cast<bf16x4 *>(dv + vrow + col) = dutok[t];
         }
         const bf16x8 df = cat8(dtok[0], dtok[1]);
-        delf[p] = cat8(deltok[0], deltok[1]);
-        duf[p] = cat8(dutok[0], dutok[1]);
-        dpa = mfma_16x16x32(df, delf[p], dpa);                                 // dO Delta^T
+        const bf16x8 delp = cat8(deltok[0], deltok[1]);
+        L.delf[p][lane] = delp;
+        L.duf[p][lane] = cat8(dutok[0], dutok[1]);
+        dpa = mfma_16x16x32(df, delp, dpa);                                    // dO Delta^T
         dtpa = mfma_16x16x32(cat8(ddtok[0], ddtok[1]), cat8(utok[0], utok[1]), dtpa);  // dDelta U^T
     }
 
     // ================= 3. the 16 x 16 backward =================
     float dbeta_c;
-    SplitDup m_darow, m_dacol, m_dprow, m_dpcol;
     {
         f32x4 dpm, tcolT;
 #pragma unroll
@@ -343,13 +344,6 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         dbeta_c = db1 + db2;
         *reinterpret_cast<f32x4 *>(&L.dat[c * 16 + 4 * grp]) = dat;
         wave_sync();
-        f32x4 dacol;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dacol[j] = L.dat[(4 * grp + j) * 16 + c];
-        m_darow = split_dup(dat);
-        m_dacol = split_dup(dacol);
-        m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
-        m_dpcol = split_dup(dpm);
     }
     if (grp == 0 && row_ok) dbeta[(size_t)tok * H + h] = dbeta_c;
 
@@ -361,8 +355,9 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         float dgam[2] = {0.f, 0.f};  // key 32ks + 16hf + c, this lane group's columns
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) dqp[hf] = dkp[hf] = dkd[hf] = zero4();
-#pragma unroll
+#pragma unroll 1
         for (int p = 0; p < 4; ++p) {
+            const bf16x8 delp = L.delf[p][lane], dup_ = L.duf[p][lane];
             const bf16x8 sa = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p) * 4 + ks) * 1024);
             const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p + 1) * 4 + ks) * 1024);
             const bf16x8 ra = *reinterpret_cast<const bf16x8 *>(Rs + ((2 * p) * 4 + ks) * 1024);
@@ -385,10 +380,21 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
                 const bf16x8 st = cat8(to_bf16x4(sta), to_bf16x4(stb));
                 const bf16x8 rt = cat8(to_bf16x4(rta), to_bf16x4(rtb));
                 dqp[hf] = mfma_16x16x32(st, df, dqp[hf]);      // (dO S0^T)^T
-                dkp[hf] = mfma_16x16x32(st, duf[p], dkp[hf]);  // (dU S0^T)^T
-                dkd[hf] = mfma_16x16x32(rt, delf[p], dkd[hf]); // (Delta R^T)^T
+                dkp[hf] = mfma_16x16x32(st, dup_, dkp[hf]);  // (dU S0^T)^T
+                dkd[hf] = mfma_16x16x32(rt, delp, dkd[hf]);  // (Delta R^T)^T
             }
         }
+        // dA~ and dP rows and columns, two bf16 terms each (from LDS, for this slab)
+        f32x4 dacol, dpcol;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dacol[j] = L.dat[(4 * grp + j) * 16 + c];
+            dpcol[j] = L.dp[(4 * grp + j) * 16 + c];
+        }
+        const SplitDup m_darow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dat[c * 16 + 4 * grp]));
+        const SplitDup m_dacol = split_dup(dacol);
+        const SplitDup m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
+        const SplitDup m_dpcol = split_dup(dpcol);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int kt = 2 * ks + hf;  // channels 16kt + 4grp + i of token c

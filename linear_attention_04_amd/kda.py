@@ -34,6 +34,10 @@ EXPORTS = (
     "kda_decode_step",
     "kda_backward_workspace_bytes",
     "kda_chunk_prefill_backward",
+    "kda_backward_records",
+    "kda_backward_states",
+    "kda_backward_state_grad",
+    "kda_backward_token_grad",
     "kda_status_string",
     "kda_version",
 )
@@ -86,6 +90,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_backward_workspace_bytes.restype = sz
     lib.kda_chunk_prefill_backward.argtypes = [p] * 15 + [dims_p, p, sz, p]
     lib.kda_chunk_prefill_backward.restype = i32
+    lib.kda_backward_records.argtypes = [p] * 5 + [dims_p, p, sz, p]
+    lib.kda_backward_records.restype = i32
+    lib.kda_backward_states.argtypes = [p] * 3 + [dims_p, p, sz, p]
+    lib.kda_backward_states.restype = i32
+    lib.kda_backward_state_grad.argtypes = [p] * 4 + [dims_p, p, sz, p]
+    lib.kda_backward_state_grad.restype = i32
+    lib.kda_backward_token_grad.argtypes = [p] * 12 + [dims_p, p, sz, p]
+    lib.kda_backward_token_grad.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -139,6 +151,30 @@ def kda_chunk_prefill_backward(q, k, v, g, beta, cu_seqlens, initial_state, d_ou
                                                          d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
                                                          ctypes.byref(dims), workspace, workspace_bytes,
                                                          stream))
+
+
+def kda_backward_records(q, k, g, beta, cu_seqlens, dims: KdaDims, workspace, workspace_bytes: int,
+                         stream) -> int:
+    return int(load_library().kda_backward_records(q, k, g, beta, cu_seqlens, ctypes.byref(dims), workspace,
+                                                   workspace_bytes, stream))
+
+
+def kda_backward_states(v, cu_seqlens, initial_state, dims: KdaDims, workspace, workspace_bytes: int,
+                        stream) -> int:
+    return int(load_library().kda_backward_states(v, cu_seqlens, initial_state, ctypes.byref(dims), workspace,
+                                                  workspace_bytes, stream))
+
+
+def kda_backward_state_grad(d_out, cu_seqlens, d_final_state, d_initial_state, dims: KdaDims, workspace,
+                            workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_backward_state_grad(d_out, cu_seqlens, d_final_state, d_initial_state,
+                                                      ctypes.byref(dims), workspace, workspace_bytes, stream))
+
+
+def kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta, dims: KdaDims,
+                            workspace, workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta,
+                                                      ctypes.byref(dims), workspace, workspace_bytes, stream))
 
 
 def kda_status_string(status: int) -> str:

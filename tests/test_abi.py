@@ -152,3 +152,20 @@ def test_backward_argument_checks(lib):
     assert kda.kda_chunk_prefill_backward(*ok, dims(N=2), p, 1 << 40, None) == kda.KDA_ERR_ARG
     assert kda.kda_chunk_prefill_backward(*ok, dims(io=kda.KDA_IO_F32, K=16, V=16), p, 1 << 40, None) == \
         kda.KDA_ERR_UNSUPPORTED
+
+
+def test_backward_stage_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    d = dims()
+    need = kda.kda_backward_workspace_bytes(d)
+    assert kda.kda_backward_records(None, p, p, p, None, d, p, need, None) == kda.KDA_ERR_ARG
+    assert kda.kda_backward_records(p, p, p, p, None, d, p, need - 1, None) == kda.KDA_ERR_WORKSPACE
+    assert kda.kda_backward_states(None, None, None, d, p, need, None) == kda.KDA_ERR_ARG
+    assert kda.kda_backward_states(p, None, b.at(4), d, p, need, None) == kda.KDA_ERR_ALIGN
+    assert kda.kda_backward_state_grad(None, None, None, None, d, p, need, None) == kda.KDA_ERR_ARG
+    assert kda.kda_backward_state_grad(p, None, p, b.at(8), d, p, need, None) == kda.KDA_ERR_ALIGN
+    assert kda.kda_backward_token_grad(p, p, p, p, p, p, None, p, p, None, p, p, d, p, need, None) == \
+        kda.KDA_ERR_ARG
+    assert kda.kda_backward_token_grad(*([p] * 6), None, *([p] * 5), dims(K=64, V=64), p, need, None) == \
+        kda.KDA_ERR_UNSUPPORTED

@@ -121,3 +121,31 @@ def test_backward_all_sequences_empty():
     r = kda.chunk_prefill_backward(q, q, q, g, beta, q, cu_seqlens=cu, d_final_state=d_fs)
     torch.cuda.synchronize()
     assert torch.equal(r["d_initial_state"], d_fs)
+
+
+def test_backward_stages_equal_one_call():
+    """The four stage calls on one workspace give the one-call results bitwise."""
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+
+    w, x, d_out, d_fs = _case("bwd_stages", 125, H=3, lengths=[33, 0, 70])
+    d = gu.upload_backward(x, d_out, d_fs, True)
+    one = gu.run_gpu_backward(d)
+    dims = kda.make_dims(d["q"], d["v"], d["cu_seqlens"], g=d["g"])
+    nbytes = kda.kda_backward_workspace_bytes(dims)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = {n: torch.empty_like(one[n]) for n in one}
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    s = torch.cuda.current_stream().cuda_stream
+    assert kda.kda_backward_records(P(d["q"]), P(d["k"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]), dims,
+                                    P(ws), nbytes, s) == 0
+    assert kda.kda_backward_states(P(d["v"]), P(d["cu_seqlens"]), P(d["initial_state"]), dims, P(ws), nbytes,
+                                   s) == 0
+    assert kda.kda_backward_state_grad(P(d["d_out"]), P(d["cu_seqlens"]), P(d["d_final_state"]),
+                                       P(out["d_initial_state"]), dims, P(ws), nbytes, s) == 0
+    assert kda.kda_backward_token_grad(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["d_out"]),
+                                       P(d["cu_seqlens"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]),
+                                       P(out["dbeta"]), dims, P(ws), nbytes, s) == 0
+    torch.cuda.synchronize()
+    for n in one:
+        assert torch.equal(out[n], one[n]), n

@@ -64,3 +64,44 @@ def test_fused_fullsize_equals_split():
     out_f, fs_f = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], fused=True)
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_f) and torch.equal(fs_s, fs_f)
+
+
+def _backward_fullsize(name, keep, w=None):
+    """The backward at a full workload: one kda_chunk_prefill_backward call over the
+    whole batch (as the benchmark times it); the oracle's gradients for the heads in
+    ``keep``, and over every head the identities <dq, q> = <dO, o> and
+    <dv, v> + <dS0, S0> = <dO, o> + <dS_T, S_T> against this library's own forward."""
+    w = w or inputs.WORKLOADS[name]
+    print(f"backward {name}: heads kept for the oracle {keep}", flush=True)
+    dev, host = gu.generate_on_device(w, keep)
+    d_out_h, d_fs_h = inputs.output_gradients(w)
+    dev["d_out"] = gu.to_device(d_out_h, True)
+    dev["d_final_state"] = gu.to_device(d_fs_h, False)
+    got = gu.run_gpu_backward(dev)
+    packed = w.num_seqs > 1
+    ref = oracle.backward(host["q"], host["k"], host["v"], host["g"], host["beta"],
+                          np.ascontiguousarray(d_out_h[:, keep]),
+                          cu_seqlens=host["cu_seqlens"] if packed else None, initial_state=host["initial_state"],
+                          d_final_state=np.ascontiguousarray(d_fs_h[:, keep]))
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        gu.assert_close_rel(n, gu.to_host(got[n][:, keep]), ref[n])
+    gu.assert_close_rel("d_initial_state", gu.to_host(got["d_initial_state"][:, keep]), ref["d_initial_state"])
+    out, fs = gu.run_gpu(dev)
+    f64 = lambda t: t.double()  # noqa: E731
+    l_out = float((f64(out) * f64(dev["d_out"])).sum())
+    l_all = l_out + float((fs.double() * dev["d_final_state"].double()).sum())
+    lhs_q = float((f64(got["dq"]) * f64(dev["q"])).sum())
+    lhs_v = float((f64(got["dv"]) * f64(dev["v"])).sum())
+    if dev["initial_state"] is not None:
+        lhs_v += float((got["d_initial_state"].double() * dev["initial_state"].double()).sum())
+    print(f"  <dq,q>={lhs_q:.6e} <dO,o>={l_out:.6e}  <dv,v>+<dS0,S0>={lhs_v:.6e} L={l_all:.6e}", flush=True)
+    assert abs(lhs_q - l_out) <= 1e-2 * abs(l_out)
+    assert abs(lhs_v - l_all) <= 1e-2 * abs(l_all)
+
+
+def test_backward_fullsize_sampled_heads():
+    _backward_fullsize("fixed_h64_t8192", [0, 21, 42, 63])
+
+
+def test_backward_fullsize_varlen_with_state():
+    _backward_fullsize("varlen_h96_t8192_n8", [5, 50, 95])
