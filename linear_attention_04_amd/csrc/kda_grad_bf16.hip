@@ -21,11 +21,12 @@
 // channels 16j + 4grp + i (element 4j + i); "slab" s of it is j = 2s, 2s + 1 (eight
 // bf16, the 16x16x32 operand that matches the state fragments' key order). Products
 // over the 128 keys take the state fragments as stored. Products over the 128 value
-// columns need the state with keys across lanes: a 16x16x32 MFMA against a 0/1
-// selection matrix moves a fragment's 16 keys of one half across lanes, exactly (the
-// values are bf16 and the accumulator fp32), and a 16x16x16 MFMA against the identity
-// turns a token-per-lane tile into a column-per-lane tile the same way. Every layout
-// change in this kernel is such an exact MFMA; LDS holds only the 16 x 16 matrices.
+// columns need the state with keys across lanes: half of a fragment (16 keys x 16
+// columns) taken as a 16x16x16 operand and multiplied by the identity comes out with
+// the keys across lanes, exactly (the values are bf16 and the accumulator fp32), and the
+// same identity product turns a token-per-lane tile into a column-per-lane tile. Every
+// layout change in this kernel is such an exact MFMA. Each state fragment is loaded
+// once; LDS holds the 16 x 16 matrices and the K+ and K^d operands.
 #include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -48,8 +49,8 @@ struct alignas(16) GradLds {
     float dat[256];  // dA~
     float dp[256];   // dP (i <= r)
     float beta[16];
-    bf16x8 delf[4][64];  // Delta, per 32-column slab: token c, the slab's columns (see below)
-    bf16x8 duf[4][64];   // dU, likewise
+    bf16x8 kps[4][64];  // K+ slabs (row layout, bf16), one per 32 keys
+    bf16x8 kds[4][64];  // K^d slabs
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -74,6 +75,11 @@ __device__ __forceinline__ SplitDup split_dup(f32x4 m) {
     bf16x4 h, l;
     split_bf16x4(m, h, l);
     return SplitDup{dup8(h), dup8(l)};
+}
+// Elements 4h .. 4h + 3 of an 8-element operand, as a 16x16x16 operand.
+__device__ __forceinline__ s16x4 half4(bf16x8 x, int h) {
+    const bf16x4 r = h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    return as_s16x4(r);
 }
 // [M_hi | M_lo] over the two halves of the reduction.
 __device__ __forceinline__ bf16x8 split_cat(f32x4 m) {
@@ -112,21 +118,13 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     const char *Rs = dstates + hc * kStateBytesBf16 + lane * 16;
     const float b = row_ok ? beta[(size_t)tok * H + h] : 0.f;
 
-    // exact 0/1 operands: I4 (16x16x16 B operand, identity) and Isel[hf] (16x16x32 B
-    // operand taking the keys 16 hf .. 16 hf + 15 of a state fragment's 32)
+    // the 16 x 16 identity as a 16x16x16 B operand (exact 0/1 entries)
     s16x4 I4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) I4[j] = (4 * grp + j == c) ? (short)0x3F80 : (short)0;
-    bf16x8 Isel[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            Isel[hf][e] = to_bf16(((e >> 2) == hf && 4 * grp + (e & 3) == c) ? 1.f : 0.f);
 
     // ================= 1. chunk factors (as the intra-chunk kernel) =================
-    bf16x8 kps[4], kds[4];  // K+ and K^d slabs (row layout, bf16)
-    f32x4 pcol;             // P[4grp + i][c] (i <= r kept)
+    f32x4 pcol;  // P[4grp + i][c] (i <= r kept)
     {
         float kr[32], qr[32], G[32];
 #pragma unroll
@@ -177,8 +175,8 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
                 split_pair(qr[e] * up0, qr[e + 1] * up1, qhh[u], qhl[u]);
                 split_pair(kr[e] * dn0, kr[e + 1] * dn1, kbh[u], kbl[u]);
             }
-            kds[s] = __builtin_bit_cast(bf16x8, make_uint4(kdw[0], kdw[1], kdw[2], kdw[3]));
-            kps[s] = __builtin_bit_cast(bf16x8, make_uint4(kpw[0], kpw[1], kpw[2], kpw[3]));
+            L.kds[s][lane] = __builtin_bit_cast(bf16x8, make_uint4(kdw[0], kdw[1], kdw[2], kdw[3]));
+            L.kps[s][lane] = __builtin_bit_cast(bf16x8, make_uint4(kpw[0], kpw[1], kpw[2], kpw[3]));
             const bf16x8 vkhh = __builtin_bit_cast(bf16x8, make_uint4(khh[0], khh[1], khh[2], khh[3]));
             const bf16x8 vkhl = __builtin_bit_cast(bf16x8, make_uint4(khl[0], khl[1], khl[2], khl[3]));
             const bf16x8 vkbh = __builtin_bit_cast(bf16x8, make_uint4(kbh[0], kbh[1], kbh[2], kbh[3]));
@@ -231,67 +229,78 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     const bf16x8 tbc = split_cat(tcol);
     const bf16x8 pc = split_cat(pcol);
 
-    // ================= 2. products over the keys, per 32-column value slab =================
+    // ================= 2. per 16-column value tile: products over the keys, then over the values ====
+    // Each state fragment is loaded once: the tile's eight fragments (S0 and R, four key
+    // slabs) serve the products over the keys as stored and, moved across lanes by the
+    // selection MFMAs, this tile's share of the products over the values.
     f32x4 dpa = zero4(), dtpa = zero4();  // dP[4grp + i][c], dT'[4grp + i][c]
-#pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-        f32x4 ksv[2], kst[2], xv[2], xt[2];
+    f32x4 dqp[8], dkp[8], dkd[8];         // (dO S0^T)^T, (dU S0^T)^T, (Delta R^T)^T: token c, keys 16kt + 4grp + i
+    float dgam[8];                        // key 16kt + c, summed over this lane group's columns
 #pragma unroll
-        for (int t = 0; t < 2; ++t) ksv[t] = kst[t] = xv[t] = xt[t] = zero4();
+    for (int kt = 0; kt < 8; ++kt) {
+        dqp[kt] = dkp[kt] = dkd[kt] = zero4();
+        dgam[kt] = 0.f;
+    }
+#pragma unroll 1
+    for (int vt = 0; vt < 8; ++vt) {
+        bf16x8 s0f[4], rf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int off = ((2 * p + t) * 4 + ks) * 1024;
-                const bf16x8 s0f = *reinterpret_cast<const bf16x8 *>(S0 + off);
-                const bf16x8 rf = *reinterpret_cast<const bf16x8 *>(Rs + off);
-                ksv[t] = mfma_16x16x32(kps[ks], s0f, ksv[t]);  // K+ S0, column per lane
-                kst[t] = mfma_16x16x32(s0f, kps[ks], kst[t]);  // the same, token per lane
-                xv[t] = mfma_16x16x32(kds[ks], rf, xv[t]);     // K^d R
-                xt[t] = mfma_16x16x32(rf, kds[ks], xt[t]);
-            }
+            s0f[ks] = *reinterpret_cast<const bf16x8 *>(S0 + (vt * 4 + ks) * 1024);
+            rf[ks] = *reinterpret_cast<const bf16x8 *>(Rs + (vt * 4 + ks) * 1024);
         }
-        bf16x4 dtok[2], utok[2], deltok[2], ddtok[2], dutok[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int col = 16 * (2 * p + t) + 4 * grp;
-            bf16x4 vt4 = {}, dt4 = {};
-            if (row_ok) {
-                vt4 = *reinterpret_cast<const bf16x4 *>(v + vrow + col);
-                dt4 = *reinterpret_cast<const bf16x4 *>(dout + vrow + col);
-            }
-            // column per lane: V[4grp + i][16t' + c], dO likewise (identity MFMA, exact)
-            const f32x4 vcol = mfma_16x16x16(as_s16x4(vt4), I4, zero4());
-            const f32x4 dcol = mfma_16x16x16(as_s16x4(dt4), I4, zero4());
-            const f32x4 ucol = vcol - ksv[t];                 // U, column per lane
-            const f32x4 utk = bf16x4_to_f32(vt4) - kst[t];    // U, token per lane
-            bf16x4 uh, ul;
-            split_bf16x4(ucol, uh, ul);
-            // Delta^T = U^T T'^T: token per lane
-            f32x4 del = mfma_16x16x32(dup8(uh), tbr, zero4());
-            del = mfma_16x16x32(dup8(ul), tbr, del);
-            const bf16x8 dcd = dup8(to_bf16x4(dcol));  // dO column tile (exact)
-            // dDelta = P^T dO + K^d R, column per lane and token per lane
-            const f32x4 ddc = mfma_16x16x32(pc, dcd, xv[t]);
-            const f32x4 ddt = mfma_16x16x32(dcd, pc, xt[t]);
-            // dU^T = dDelta^T T': token per lane
-            bf16x4 dh, dl;
-            split_bf16x4(ddc, dh, dl);
-            f32x4 du = mfma_16x16x32(dup8(dh), tbc, zero4());
-            du = mfma_16x16x32(dup8(dl), tbc, du);
-            dtok[t] = dt4;
-            utok[t] = to_bf16x4(utk);
-            deltok[t] = to_bf16x4(del);
-            ddtok[t] = to_bf16x4(ddt);
-            dutok[t] = to_bf16x4(du);
-            if (row_ok) *reinterpret_cast<bf16x4 *>(dv + vrow + col) = dutok[t];
+        const int col = 16 * vt + 4 * grp;
+        bf16x4 vt4 = {}, dt4 = {};
+        if (row_ok) {
+            vt4 = *reinterpret_cast<const bf16x4 *>(v + vrow + col);
+            dt4 = *reinterpret_cast<const bf16x4 *>(dout + vrow + col);
         }
-        const bf16x8 df = cat8(dtok[0], dtok[1]);
-        const bf16x8 delp = cat8(deltok[0], deltok[1]);
-        L.delf[p][lane] = delp;
-        L.duf[p][lane] = cat8(dutok[0], dutok[1]);
-        dpa = mfma_16x16x32(df, delp, dpa);                                    // dO Delta^T
-        dtpa = mfma_16x16x32(cat8(ddtok[0], ddtok[1]), cat8(utok[0], utok[1]), dtpa);  // dDelta U^T
+        f32x4 ksv = zero4(), kst = zero4(), xv = zero4(), xt = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 kp = L.kps[ks][lane], kd = L.kds[ks][lane];
+            ksv = mfma_16x16x32(kp, s0f[ks], ksv);  // K+ S0, column per lane
+            kst = mfma_16x16x32(s0f[ks], kp, kst);  // the same, token per lane
+            xv = mfma_16x16x32(kd, rf[ks], xv);     // K^d R
+            xt = mfma_16x16x32(rf[ks], kd, xt);
+        }
+        // column per lane: V[4grp + i][16vt + c], dO likewise (identity MFMA, exact)
+        const f32x4 vcol = mfma_16x16x16(as_s16x4(vt4), I4, zero4());
+        const f32x4 dcol = mfma_16x16x16(as_s16x4(dt4), I4, zero4());
+        const f32x4 ucol = vcol - ksv;               // U, column per lane
+        const f32x4 utk = bf16x4_to_f32(vt4) - kst;  // U, token per lane
+        bf16x4 uh, ul;
+        split_bf16x4(ucol, uh, ul);
+        // Delta^T = U^T T'^T: token per lane
+        f32x4 del = mfma_16x16x32(dup8(uh), tbr, zero4());
+        del = mfma_16x16x32(dup8(ul), tbr, del);
+        const bf16x8 dcd = dup8(to_bf16x4(dcol));  // dO column tile (exact)
+        // dDelta = P^T dO + K^d R, column per lane and token per lane
+        const f32x4 ddc = mfma_16x16x32(pc, dcd, xv);
+        const f32x4 ddt = mfma_16x16x32(dcd, pc, xt);
+        // dU^T = dDelta^T T': token per lane
+        bf16x4 dh, dl;
+        split_bf16x4(ddc, dh, dl);
+        f32x4 du = mfma_16x16x32(dup8(dh), tbc, zero4());
+        du = mfma_16x16x32(dup8(dl), tbc, du);
+        const bf16x4 utok = to_bf16x4(utk), deltok = to_bf16x4(del), ddtok = to_bf16x4(ddt);
+        const bf16x4 dutok = to_bf16x4(du);
+        if (row_ok) *reinterpret_cast<bf16x4 *>(dv + vrow + col) = dutok;
+        dpa = mfma_16x16x16(as_s16x4(dt4), as_s16x4(deltok), dpa);     // dO Delta^T
+        dtpa = mfma_16x16x16(as_s16x4(ddtok), as_s16x4(utok), dtpa);   // dDelta U^T
+        // products over this tile's 16 columns, for all 128 keys
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            // key 16kt + c across lanes, columns 16vt + 4grp + i: the fragment's half
+            // (kt & 1) as a 16x16x16 operand (rows: columns of S), times the identity
+            const f32x4 st = mfma_16x16x16(half4(s0f[kt >> 1], kt & 1), I4, zero4());
+            const f32x4 rt = mfma_16x16x16(half4(rf[kt >> 1], kt & 1), I4, zero4());
+            dgam[kt] += st[0] * rt[0] + st[1] * rt[1] + st[2] * rt[2] + st[3] * rt[3];
+            const s16x4 stb = as_s16x4(to_bf16x4(st)), rtb = as_s16x4(to_bf16x4(rt));
+            dqp[kt] = mfma_16x16x16(stb, as_s16x4(dt4), dqp[kt]);
+            dkp[kt] = mfma_16x16x16(stb, as_s16x4(dutok), dkp[kt]);
+            dkd[kt] = mfma_16x16x16(rtb, as_s16x4(deltok), dkd[kt]);
+        }
     }
 
     // ================= 3. the 16 x 16 backward =================
@@ -347,129 +356,92 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     }
     if (grp == 0 && row_ok) dbeta[(size_t)tok * H + h] = dbeta_c;
 
-    // ================= 4. per 32-key slab: products over the values, then dq, dk, dg =================
+    // ================= 4. per 16-channel key tile: dq, dk, dg =================
     float dgs = 0.f;  // scalar gate: sum of dg over this lane's channels
-#pragma unroll 1
-    for (int ks = 0; ks < 4; ++ks) {
-        f32x4 dqp[2], dkp[2], dkd[2];
-        float dgam[2] = {0.f, 0.f};  // key 32ks + 16hf + c, this lane group's columns
+    f32x4 dacol, dpcol;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) dqp[hf] = dkp[hf] = dkd[hf] = zero4();
-#pragma unroll 1
-        for (int p = 0; p < 4; ++p) {
-            const bf16x8 delp = L.delf[p][lane], dup_ = L.duf[p][lane];
-            const bf16x8 sa = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p) * 4 + ks) * 1024);
-            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(S0 + ((2 * p + 1) * 4 + ks) * 1024);
-            const bf16x8 ra = *reinterpret_cast<const bf16x8 *>(Rs + ((2 * p) * 4 + ks) * 1024);
-            const bf16x8 rb = *reinterpret_cast<const bf16x8 *>(Rs + ((2 * p + 1) * 4 + ks) * 1024);
-            bf16x4 d0 = {}, d1 = {};
-            if (row_ok) {
-                d0 = *reinterpret_cast<const bf16x4 *>(dout + vrow + 32 * p + 4 * grp);
-                d1 = *reinterpret_cast<const bf16x4 *>(dout + vrow + 32 * p + 16 + 4 * grp);
-            }
-            const bf16x8 df = cat8(d0, d1);
+    for (int j = 0; j < 4; ++j) {
+        dacol[j] = L.dat[(4 * grp + j) * 16 + c];
+        dpcol[j] = L.dp[(4 * grp + j) * 16 + c];
+    }
+    // dA~ and dP rows and columns, two bf16 terms each
+    const SplitDup m_darow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dat[c * 16 + 4 * grp]));
+    const SplitDup m_dacol = split_dup(dacol);
+    const SplitDup m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
+    const SplitDup m_dpcol = split_dup(dpcol);
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                // key 32ks + 16hf + c across lanes, columns 32p + 4grp + i and 32p + 16 + 4grp + i
-                const f32x4 sta = mfma_16x16x32(sa, Isel[hf], zero4());
-                const f32x4 stb = mfma_16x16x32(sb, Isel[hf], zero4());
-                const f32x4 rta = mfma_16x16x32(ra, Isel[hf], zero4());
-                const f32x4 rtb = mfma_16x16x32(rb, Isel[hf], zero4());
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dgam[hf] += sta[i] * rta[i] + stb[i] * rtb[i];
-                const bf16x8 st = cat8(to_bf16x4(sta), to_bf16x4(stb));
-                const bf16x8 rt = cat8(to_bf16x4(rta), to_bf16x4(rtb));
-                dqp[hf] = mfma_16x16x32(st, df, dqp[hf]);      // (dO S0^T)^T
-                dkp[hf] = mfma_16x16x32(st, dup_, dkp[hf]);  // (dU S0^T)^T
-                dkd[hf] = mfma_16x16x32(rt, delp, dkd[hf]);  // (Delta R^T)^T
+    for (int kt = 0; kt < 8; ++kt) {
+        const size_t kc = krow + 16 * kt + 4 * grp;  // channels 16kt + 4grp + i of token c
+        f32x4 kk = zero4(), qq = zero4(), G = zero4();
+        if (row_ok) {
+            kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(k + kc));
+            qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(q + kc));
+            if (SCALAR_GATE) {
+                const float gs = g[(size_t)tok * H + h];
+                G = f32x4{gs, gs, gs, gs};
+            } else {
+                const float4 gv = *reinterpret_cast<const float4 *>(g + kc);
+                G = f32x4{gv.x, gv.y, gv.z, gv.w};
             }
         }
-        // dA~ and dP rows and columns, two bf16 terms each (from LDS, for this slab)
-        f32x4 dacol, dpcol;
+        f32x4 up, dn, eg, ed, gam, khat, qhat, krev;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dacol[j] = L.dat[(4 * grp + j) * 16 + c];
-            dpcol[j] = L.dp[(4 * grp + j) * 16 + c];
+        for (int i = 0; i < 4; ++i) {
+            G[i] = row_inclusive_sum(G[i]);
+            const float d = G[i] - row_bcast<7>(G[i]);
+            up[i] = __expf(d);
+            dn[i] = __expf(-d);
+            eg[i] = __expf(G[i]);
+            ed[i] = dn[i] * row_bcast<15>(up[i]);
+            gam[i] = row_bcast<15>(eg[i]);
+            khat[i] = kk[i] * up[i];
+            qhat[i] = qq[i] * up[i];
+            krev[i] = kk[i] * dn[i];
         }
-        const SplitDup m_darow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dat[c * 16 + 4 * grp]));
-        const SplitDup m_dacol = split_dup(dacol);
-        const SplitDup m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
-        const SplitDup m_dpcol = split_dup(dpcol);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int kt = 2 * ks + hf;  // channels 16kt + 4grp + i of token c
-            const size_t kc = krow + 16 * kt + 4 * grp;
-            f32x4 kk = zero4(), qq = zero4(), G = zero4();
-            if (row_ok) {
-                kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(k + kc));
-                qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(q + kc));
-                if (SCALAR_GATE) {
-                    const float gs = g[(size_t)tok * H + h];
-                    G = f32x4{gs, gs, gs, gs};
-                } else {
-                    const float4 gv = *reinterpret_cast<const float4 *>(g + kc);
-                    G = f32x4{gv.x, gv.y, gv.z, gv.w};
-                }
-            }
-            f32x4 up, dn, eg, ed, gam, khat, qhat, krev;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                G[i] = row_inclusive_sum(G[i]);
-                const float d = G[i] - row_bcast<7>(G[i]);
-                up[i] = __expf(d);
-                dn[i] = __expf(-d);
-                eg[i] = __expf(G[i]);
-                ed[i] = dn[i] * row_bcast<15>(up[i]);
-                gam[i] = row_bcast<15>(eg[i]);
-                khat[i] = kk[i] * up[i];
-                qhat[i] = qq[i] * up[i];
-                krev[i] = kk[i] * dn[i];
-            }
-            // channel per lane, [hi | lo] over tokens 4grp .. + 3 (identity MFMAs, exact)
-            auto chan_major = [&](f32x4 x) {
-                bf16x4 xh, xl;
-                split_bf16x4(x, xh, xl);
-                const f32x4 th = mfma_16x16x16(as_s16x4(xh), I4, zero4());
-                const f32x4 tl = mfma_16x16x16(as_s16x4(xl), I4, zero4());
-                return cat8(to_bf16x4(th), to_bf16x4(tl));
-            };
-            const bf16x8 krev_c = chan_major(krev), khat_c = chan_major(khat), qhat_c = chan_major(qhat);
-            f32x4 dkhat = mfma_16x16x32(krev_c, m_darow.hi, zero4());
-            dkhat = mfma_16x16x32(krev_c, m_darow.lo, dkhat);
-            f32x4 dkrev = mfma_16x16x32(khat_c, m_dacol.hi, zero4());
-            dkrev = mfma_16x16x32(khat_c, m_dacol.lo, dkrev);
-            dkrev = mfma_16x16x32(qhat_c, m_dpcol.hi, dkrev);
-            dkrev = mfma_16x16x32(qhat_c, m_dpcol.lo, dkrev);
-            f32x4 dqhat = mfma_16x16x32(krev_c, m_dprow.hi, zero4());
-            dqhat = mfma_16x16x32(krev_c, m_dprow.lo, dqhat);
+        // channel per lane, [hi | lo] over tokens 4grp .. + 3 (identity MFMAs, exact)
+        auto chan_major = [&](f32x4 x) {
+            bf16x4 xh, xl;
+            split_bf16x4(x, xh, xl);
+            const f32x4 th = mfma_16x16x16(as_s16x4(xh), I4, zero4());
+            const f32x4 tl = mfma_16x16x16(as_s16x4(xl), I4, zero4());
+            return cat8(to_bf16x4(th), to_bf16x4(tl));
+        };
+        const bf16x8 krev_c = chan_major(krev), khat_c = chan_major(khat), qhat_c = chan_major(qhat);
+        f32x4 dkhat = mfma_16x16x32(krev_c, m_darow.hi, zero4());
+        dkhat = mfma_16x16x32(krev_c, m_darow.lo, dkhat);
+        f32x4 dkrev = mfma_16x16x32(khat_c, m_dacol.hi, zero4());
+        dkrev = mfma_16x16x32(khat_c, m_dacol.lo, dkrev);
+        dkrev = mfma_16x16x32(qhat_c, m_dpcol.hi, dkrev);
+        dkrev = mfma_16x16x32(qhat_c, m_dpcol.lo, dkrev);
+        f32x4 dqhat = mfma_16x16x32(krev_c, m_dprow.hi, zero4());
+        dqhat = mfma_16x16x32(krev_c, m_dprow.lo, dqhat);
 
-            // dgamma for this lane's four channels: sum over the lane groups, then
-            // channel 16kt + 4grp + i sits in lane 4grp + i
-            float dgt = dgam[hf];
-            dgt += __shfl_xor(dgt, 16, 64);
-            dgt += __shfl_xor(dgt, 32, 64);
-            f32x4 dkq, dqq, dgv;
+        // dgamma for this lane's four channels: sum over the lane groups, then
+        // channel 16kt + 4grp + i sits in lane 4grp + i
+        float dgt = dgam[kt];
+        dgt += __shfl_xor(dgt, 16, 64);
+        dgt += __shfl_xor(dgt, 32, 64);
+        f32x4 dkq, dqq, dgv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float dkplus = -dkp[hf][i];
-                const float kd = kk[i] * ed[i];
-                dkq[i] = dkhat[i] * up[i] + dkrev[i] * dn[i] + dkplus * eg[i] + dkd[hf][i] * ed[i];
-                dqq[i] = dqhat[i] * up[i] + dqp[hf][i] * eg[i];
-                float dG = dkhat[i] * khat[i] - dkrev[i] * krev[i] + dqhat[i] * qhat[i] + dkplus * (kk[i] * eg[i]) +
-                           dqp[hf][i] * (qq[i] * eg[i]) - dkd[hf][i] * kd;
-                const float dgc = row_bcast<15>(row_inclusive_sum(dkd[hf][i] * kd)) +
-                                  __shfl(dgt, 4 * grp + i, 64) * gam[i];
-                if (c == len - 1) dG += dgc;
-                dgv[i] = row_suffix_sum(dG);
-            }
-            if (row_ok) {
-                *reinterpret_cast<bf16x4 *>(dk + kc) = to_bf16x4(dkq);
-                *reinterpret_cast<bf16x4 *>(dq + kc) = to_bf16x4(dqq);
-                if (SCALAR_GATE)
-                    dgs += dgv[0] + dgv[1] + dgv[2] + dgv[3];
-                else
-                    *reinterpret_cast<float4 *>(dg + kc) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float dkplus = -dkp[kt][i];
+            const float kd = kk[i] * ed[i];
+            dkq[i] = dkhat[i] * up[i] + dkrev[i] * dn[i] + dkplus * eg[i] + dkd[kt][i] * ed[i];
+            dqq[i] = dqhat[i] * up[i] + dqp[kt][i] * eg[i];
+            float dG = dkhat[i] * khat[i] - dkrev[i] * krev[i] + dqhat[i] * qhat[i] + dkplus * (kk[i] * eg[i]) +
+                       dqp[kt][i] * (qq[i] * eg[i]) - dkd[kt][i] * kd;
+            const float dgc =
+                row_bcast<15>(row_inclusive_sum(dkd[kt][i] * kd)) + __shfl(dgt, 4 * grp + i, 64) * gam[i];
+            if (c == len - 1) dG += dgc;
+            dgv[i] = row_suffix_sum(dG);
+        }
+        if (row_ok) {
+            *reinterpret_cast<bf16x4 *>(dk + kc) = to_bf16x4(dkq);
+            *reinterpret_cast<bf16x4 *>(dq + kc) = to_bf16x4(dqq);
+            if (SCALAR_GATE)
+                dgs += dgv[0] + dgv[1] + dgv[2] + dgv[3];
+            else
+                *reinterpret_cast<float4 *>(dg + kc) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
         }
     }
     if (SCALAR_GATE) {
