@@ -426,12 +426,12 @@ def main():
         "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th,
                   ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_device.h", "kda_chunks.h"]),
         "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * w.num_seqs * H * n_states,
-                  ["kda_inter_bf16.hip", "kda_device.h", "kda_chunks.h"]),
+                  ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"]),
     }
     if args.fused:
         # one launch; its algorithmic bytes are the path's compulsory bytes
-        kernels = {"fused": (intra_ms, counts["bytes"], ["kda_inter_bf16.hip", "kda_intra_wave.h", "kda_device.h",
-                                                         "kda_chunks.h"])}
+        kernels = {"fused": (intra_ms, counts["bytes"], ["kda_inter_bf16.hip", "kda_ring.h", "kda_intra_wave.h",
+                                                         "kda_device.h", "kda_chunks.h"])}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
