@@ -38,7 +38,9 @@ constexpr int KD = 128;
 constexpr int VD = 128;
 constexpr int kWaves = 4;
 
-// One wave's 16 x 16 matrices, row-major.
+// One wave's 16 x 16 matrices, row-major. The matrices and the K+/K^d area are also
+// reused to gather each output tile before it is written out in whole rows
+// (dv in dt..dp during the value tiles; dg in a..dp and dq, dk in kps/kds at the end).
 struct alignas(16) GradLds {
     float a[256];    // A = diag(beta) A~, strictly lower (the forward substitution)
     float at[256];   // A~
@@ -52,6 +54,28 @@ struct alignas(16) GradLds {
     bf16x8 kps[4][64];  // K+ slabs (row layout, bf16), one per 32 keys
     bf16x8 kds[4][64];  // K^d slabs
 };
+
+// A 16-token tile of row bytes `row` (256 or 512) in LDS, 16-byte chunks swizzled by
+// the row (chunk ^ r) so that neither the per-token writes nor the per-row reads
+// conflict in the banks.
+template <int ROW>
+__device__ __forceinline__ int tile_off(int r, int byte) {
+    return r * ROW + ((((byte >> 4) ^ r) << 4) | (byte & 15));
+}
+
+// Write the 16 x ROW-byte tile at `lds` to global rows (row r at `g0 + r * gstride`),
+// rows r < len only: each wave-wide store moves 1 KiB of whole rows.
+template <int ROW>
+__device__ __forceinline__ void store_tile(const char *lds, char *g0, size_t gstride, int len, int lane) {
+    constexpr int kLanesPerRow = ROW / 16;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll
+    for (int s = 0; s < 16 / kRowsPerStore; ++s) {
+        const int r = s * kRowsPerStore + lane / kLanesPerRow, j = lane % kLanesPerRow;
+        const uint4 x = *reinterpret_cast<const uint4 *>(lds + tile_off<ROW>(r, 16 * j));
+        if (r < len) *reinterpret_cast<uint4 *>(g0 + (size_t)r * gstride + 16 * j) = x;
+    }
+}
 
 __device__ __forceinline__ void wave_sync() {
     asm volatile("" ::: "memory");
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         du = mfma_16x16x32(dup8(dl), tbc, du);
         const bf16x4 utok = to_bf16x4(utk), deltok = to_bf16x4(del), ddtok = to_bf16x4(ddt);
         const bf16x4 dutok = to_bf16x4(du);
-        if (row_ok) *reinterpret_cast<bf16x4 *>(dv + vrow + col) = dutok;
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<char *>(L.dt) + tile_off<256>(c, 2 * col)) = dutok;
         dpa = mfma_16x16x16(as_s16x4(dt4), as_s16x4(deltok), dpa);     // dO Delta^T
         dtpa = mfma_16x16x16(as_s16x4(ddtok), as_s16x4(utok), dtpa);   // dDelta U^T
         // products over this tile's 16 columns, for all 128 keys
@@ -302,6 +326,11 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             dkd[kt] = mfma_16x16x16(rtb, as_s16x4(deltok), dkd[kt]);
         }
     }
+
+    wave_sync();
+    store_tile<256>(reinterpret_cast<const char *>(L.dt), reinterpret_cast<char *>(dv + ((size_t)start * H + h) * VD),
+                    (size_t)H * VD * 2, len, lane);
+    wave_sync();
 
     // ================= 3. the 16 x 16 backward =================
     float dbeta_c;
@@ -369,6 +398,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     const SplitDup m_dacol = split_dup(dacol);
     const SplitDup m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
     const SplitDup m_dpcol = split_dup(dpcol);
+    wave_sync();  // the matrices' area now gathers dg, the K+/K^d area dq and dk
+    char *tg = reinterpret_cast<char *>(L.a);
+    char *tq = reinterpret_cast<char *>(L.kps);
+    char *tk = reinterpret_cast<char *>(L.kds);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
         const size_t kc = krow + 16 * kt + 4 * grp;  // channels 16kt + 4grp + i of token c
@@ -435,15 +468,20 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             if (c == len - 1) dG += dgc;
             dgv[i] = row_suffix_sum(dG);
         }
-        if (row_ok) {
-            *reinterpret_cast<bf16x4 *>(dk + kc) = to_bf16x4(dkq);
-            *reinterpret_cast<bf16x4 *>(dq + kc) = to_bf16x4(dqq);
-            if (SCALAR_GATE)
-                dgs += dgv[0] + dgv[1] + dgv[2] + dgv[3];
-            else
-                *reinterpret_cast<float4 *>(dg + kc) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
+        const int cb = 2 * (16 * kt + 4 * grp);  // byte of channel 16kt + 4grp in a bf16 row
+        *reinterpret_cast<bf16x4 *>(tk + tile_off<256>(c, cb)) = to_bf16x4(dkq);
+        *reinterpret_cast<bf16x4 *>(tq + tile_off<256>(c, cb)) = to_bf16x4(dqq);
+        if (SCALAR_GATE) {
+            if (row_ok) dgs += dgv[0] + dgv[1] + dgv[2] + dgv[3];
+        } else {
+            *reinterpret_cast<f32x4 *>(tg + tile_off<512>(c, 2 * cb)) = dgv;
         }
     }
+    wave_sync();
+    const size_t row0 = ((size_t)start * H + h) * KD;
+    store_tile<256>(tk, reinterpret_cast<char *>(dk + row0), (size_t)H * KD * 2, len, lane);
+    store_tile<256>(tq, reinterpret_cast<char *>(dq + row0), (size_t)H * KD * 2, len, lane);
+    if (!SCALAR_GATE) store_tile<512>(tg, reinterpret_cast<char *>(dg + row0), (size_t)H * KD * 4, len, lane);
     if (SCALAR_GATE) {
         dgs += __shfl_xor(dgs, 16, 64);
         dgs += __shfl_xor(dgs, 32, 64);
