@@ -270,8 +270,8 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         bf16x8 s0f[4], rf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            s0f[ks] = *reinterpret_cast<const bf16x8 *>(S0 + (vt * 4 + ks) * 1024);
-            rf[ks] = *reinterpret_cast<const bf16x8 *>(Rs + (vt * 4 + ks) * 1024);
+            s0f[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(S0 + (vt * 4 + ks) * 1024));
+            rf[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(Rs + (vt * 4 + ks) * 1024));
         }
         const int col = 16 * vt + 4 * grp;
         bf16x4 vt4 = {}, dt4 = {};

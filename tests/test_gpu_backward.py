@@ -149,3 +149,49 @@ def test_backward_stages_equal_one_call():
     torch.cuda.synchronize()
     for n in one:
         assert torch.equal(out[n], one[n]), n
+
+
+def test_backward_graph_replay():
+    """kda_chunk_prefill_backward (packed sequences) captured once in a HIP graph and
+    replayed with new inputs, eager work and synchronisation between replays; every
+    replay equals an eager call on fresh buffers, bitwise."""
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+
+    lengths = [40, 0, 77, 16]
+    w, x, d_out, d_fs = _case("bwd_graph_a", 130, H=3, lengths=lengths)
+    d = gu.upload_backward(x, d_out, d_fs, True)
+    dims = kda.make_dims(d["q"], d["v"], d["cu_seqlens"], g=d["g"])
+    nbytes = kda.kda_backward_workspace_bytes(dims)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    outs = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+                dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+                d_initial_state=torch.empty_like(d["initial_state"]))
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    def call():
+        st = kda.kda_chunk_prefill_backward(
+            P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]), P(d["initial_state"]),
+            P(d["d_out"]), P(d["d_final_state"]), P(outs["dq"]), P(outs["dk"]), P(outs["dv"]), P(outs["dg"]),
+            P(outs["dbeta"]), P(outs["d_initial_state"]), dims, P(ws), nbytes,
+            torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _, xr, dor, dfr = _case(f"bwd_graph_r{rep}", 131 + rep, H=3, lengths=lengths)
+        dr = gu.upload_backward(xr, dor, dfr, True)
+        for name in ("q", "k", "v", "g", "beta", "initial_state", "d_out", "d_final_state"):
+            d[name].copy_(dr[name])
+        ref = gu.run_gpu_backward(dr)  # eager, on fresh buffers and a fresh workspace
+        for t in outs.values():
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(t, ref[name]), f"replay {rep}: {name} differs from the eager call"
