@@ -131,16 +131,17 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
         o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + ((2 * KH + s) * 64 + lane) * 16);
         o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + ((2 * KH + s) * 64 + lane) * 16);
     }
-    // the same 8 bytes read twice from LDS (an opaque offset keeps the two reads
-    // apart) instead of duplicating registers
+    // the same 8 bytes read twice from LDS (volatile LDS reads are not merged into
+    // one) instead of duplicating registers
+    typedef const volatile __attribute__((address_space(3))) unsigned long long lds_u64;
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
         const int m = 4 * KH + mm;
-        int off = kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8;
-        const uint2 a = *reinterpret_cast<const uint2 *>(slot + off);
-        asm volatile("" : "+v"(off));
-        const uint2 b = *reinterpret_cast<const uint2 *>(slot + off);
-        o.kd[mm] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+        lds_u64 *pk = (lds_u64 *)(slot + kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8);
+        const unsigned long long a = *pk;
+        const unsigned long long b = *pk;
+        o.kd[mm] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b,
+                                                         (unsigned)(b >> 32)));
     }
     o.tv = *reinterpret_cast<const bf16x8 *>(slot + (KH ? kRecTB : kRecMM) + lane * 16);
     o.gam = *reinterpret_cast<const float2 *>(slot + kRecGAM + (grp * 32 + 2 * c) * 4);
@@ -219,12 +220,10 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
     const f32x4 x0 = KH == 0 ? x : px;
     const f32x4 z1 = KH == 0 ? px : x;
     const f32x4 d = -(x0 + z1);
-    bf16x8 db;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        db[i] = to_bf16(d[i]);
-        db[4 + i] = to_bf16(d[i] - from_bf16(db[i]));
-    }
+    unsigned int h01, h23, l01, l23;  // Delta = hi + lo, packed pairs
+    split_pair(d[0], d[1], h01, l01);
+    split_pair(d[2], d[3], h23, l23);
+    const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) S[mm] = mfma_16x16x32(o.kd[mm], db, S[mm]);  // K^d^T (Delta_hi + Delta_lo)
     if (KH == 0 && !SAVE) {

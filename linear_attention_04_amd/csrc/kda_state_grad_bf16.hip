@@ -91,15 +91,18 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
 #pragma unroll
     for (int s = 0; s < 2; ++s)
         o.kd[s] = *reinterpret_cast<const bf16x8 *>(slot + kBRecKD + ((2 * KH + s) * 64 + lane) * 16);
+    // W^T: the same 8 bytes read twice from LDS (volatile LDS reads are not merged into
+    // one) instead of duplicating registers
+    typedef const volatile __attribute__((address_space(3))) unsigned long long lds_u64;
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
         const int m = 4 * KH + mm;
         const int base = ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8;
-        int off = kBRecWT + base;
-        const uint2 a = *reinterpret_cast<const uint2 *>(slot + off);
-        asm volatile("" : "+v"(off));  // a second read of the same bytes, not a register copy
-        const uint2 b = *reinterpret_cast<const uint2 *>(slot + off);
-        o.wt[mm] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+        lds_u64 *pw = (lds_u64 *)(slot + kBRecWT + base);
+        const unsigned long long a = *pw;
+        const unsigned long long b = *pw;
+        o.wt[mm] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b,
+                                                         (unsigned)(b >> 32)));
         o.qt[mm] = *reinterpret_cast<const s16x4 *>(slot + kBRecQT + base);
     }
     o.gam = *reinterpret_cast<const float2 *>(slot + kGamOff + (grp * 32 + 2 * c) * 4);
@@ -146,12 +149,10 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&R)[4], co
     const f32x4 x0 = KH == 0 ? x : px;
     const f32x4 x1 = KH == 0 ? px : x;
     const f32x4 d = -(x0 + x1);
-    bf16x8 db;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        db[i] = to_bf16(d[i]);
-        db[4 + i] = to_bf16(d[i] - from_bf16(db[i]));
-    }
+    unsigned int h01, h23, l01, l23;  // -X = hi + lo, packed pairs
+    split_pair(d[0], d[1], h01, l01);
+    split_pair(d[2], d[3], h23, l23);
+    const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) R[mm] = mfma_16x16x32(o.wt[mm], db, R[mm]);
 }
