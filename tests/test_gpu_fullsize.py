@@ -105,3 +105,13 @@ def test_backward_fullsize_sampled_heads():
 
 def test_backward_fullsize_varlen_with_state():
     _backward_fullsize("varlen_h96_t8192_n8", [5, 50, 95])
+
+
+def test_backward_fullsize_h96_with_state():
+    _backward_fullsize("fixed_h96_t8192_s0", [0, 47, 95])
+
+
+def test_backward_fullsize_long_context_sampled_heads():
+    """131 072 tokens of 64 heads (about 60 GB of device memory with the workspace's
+    chunk states); the oracle evaluates two heads."""
+    _backward_fullsize("long_h64_t131072_s0", [7, 56])
