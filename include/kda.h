@@ -211,6 +211,21 @@ int kda_backward_token_grad(const void *q, const void *k, const void *v, const f
                             const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* Checks packed-sequence boundaries on the device (the other entry points never read
+ * them on the host; their kernels clamp every boundary they read, so malformed ones
+ * give wrong numbers, never out-of-range accesses). Sequences are packed back to back
+ * as in the variable-length column of the FlashKDA benchmark (tech-noisy.com, section
+ * "MoE通信とアテンション:MoonEPとFlashKDA").
+ *   cu_seqlens [num_seqs + 1] int32, device, 4-byte aligned
+ *   result     one int32, device, 4-byte aligned: written with the smallest n in
+ *              [0, num_seqs] at which cu_seqlens[0] = 0, cu_seqlens[n - 1] <=
+ *              cu_seqlens[n] or cu_seqlens[num_seqs] = total_tokens fails, else -1.
+ * Asynchronous on `stream` like every entry point: read *result after the stream has
+ * passed the call. KDA_ERR_ARG for NULL pointers, num_seqs outside [1, 2^24] or
+ * total_tokens outside [0, 2^31 - 1]; KDA_ERR_ALIGN for misaligned pointers. */
+int kda_check_seqlens(const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t *result,
+                      void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);
 

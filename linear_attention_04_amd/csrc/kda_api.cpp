@@ -301,12 +301,23 @@ int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, cons
     return st;
 }
 
+int kda_check_seqlens(const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t *result,
+                      void *stream) {
+    if (cu_seqlens == nullptr || result == nullptr) return KDA_ERR_ARG;
+    if (num_seqs < 1 || num_seqs > (1 << 24) || total_tokens < 0 || total_tokens > (int64_t)INT32_MAX)
+        return KDA_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(result) & 3u) != 0)
+        return KDA_ERR_ALIGN;
+    return kda::launch_status(
+        kda::launch_check_seqlens(cu_seqlens, num_seqs, total_tokens, result, static_cast<hipStream_t>(stream)));
+}
+
 const char *kda_status_string(int status) {
     switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_ARG: return "invalid argument (NULL pointer, bad sizes, or num_seqs != 1 without cu_seqlens)";
     case KDA_ERR_UNSUPPORTED: return "unsupported head size / io dtype combination";
-    case KDA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case KDA_ERR_ALIGN: return "a data pointer is misaligned (16 bytes; 4 for int32 arrays)";
     case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_workspace_bytes()";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";

@@ -6,6 +6,8 @@
 // computes chunk_off[n] = sum over m < n of ceil(len_m / 16) with a block-wide scan,
 // then labels every chunk slot with its sequence by binary search over chunk_off.
 // It runs on the device so that no host synchronisation is needed.
+#include <climits>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -67,6 +69,36 @@ hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, vo
     int32_t *chunk_seq = reinterpret_cast<int32_t *>(base + geo.off_chunk_seq);
     hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(kTableThreads), 0, stream, cu_seqlens,
                        geo.N, geo.T, geo.max_chunks, chunk_off, chunk_seq);
+    return hipGetLastError();
+}
+
+
+// Check of packed-sequence boundaries, which the host never reads: the smallest n in
+// [0, N] at which cu[0] = 0, cu[n - 1] <= cu[n] or cu[N] = T fails, else -1. The
+// prefill kernels do not depend on it (they clamp every boundary they read); it lets
+// a caller find malformed boundaries that would otherwise only give wrong numbers.
+__global__ __launch_bounds__(kTableThreads) void kda_check_seqlens_kernel(const int32_t *__restrict__ cu, int N,
+                                                                          int64_t T, int32_t *__restrict__ result) {
+    __shared__ int first;
+    const int tid = threadIdx.x;
+    if (tid == 0) first = INT_MAX;
+    __syncthreads();
+    for (int n = tid; n <= N; n += kTableThreads) {
+        const int64_t x = cu[n];
+        const bool bad = (n == 0 ? x != 0 : x < (int64_t)cu[n - 1]) || (n == N && x != T);
+        if (bad) {
+            atomicMin(&first, n);  // n grows along the loop: this thread's first failure is its smallest
+            break;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) *result = first == INT_MAX ? -1 : first;
+}
+
+hipError_t launch_check_seqlens(const int32_t *cu_seqlens, int num_seqs, int64_t total_tokens, int32_t *result,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(kda_check_seqlens_kernel, dim3(1), dim3(kTableThreads), 0, stream, cu_seqlens, num_seqs,
+                       total_tokens, result);
     return hipGetLastError();
 }
 

@@ -75,6 +75,8 @@ int make_geometry(const kda_dims_t *d, Geometry *g);
 // make_geometry plus the backward pass's workspace areas (bf16 io only).
 int make_backward_geometry(const kda_dims_t *d, Geometry *g);
 
+hipError_t launch_check_seqlens(const int32_t *cu_seqlens, int num_seqs, int64_t total_tokens, int32_t *result,
+                                hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, void *ws,
                               hipStream_t stream);
 hipError_t launch_intra_bf16(const void *q, const void *k, const float *g, const float *beta,

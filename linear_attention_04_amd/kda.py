@@ -38,6 +38,7 @@ EXPORTS = (
     "kda_backward_states",
     "kda_backward_state_grad",
     "kda_backward_token_grad",
+    "kda_check_seqlens",
     "kda_status_string",
     "kda_version",
 )
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_backward_state_grad.restype = i32
     lib.kda_backward_token_grad.argtypes = [p] * 12 + [dims_p, p, sz, p]
     lib.kda_backward_token_grad.restype = i32
+    lib.kda_check_seqlens.argtypes = [p, ctypes.c_int32, ctypes.c_int64, p, p]
+    lib.kda_check_seqlens.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -175,6 +178,10 @@ def kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg,
                             workspace, workspace_bytes: int, stream) -> int:
     return int(load_library().kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta,
                                                       ctypes.byref(dims), workspace, workspace_bytes, stream))
+
+
+def kda_check_seqlens(cu_seqlens, num_seqs: int, total_tokens: int, result, stream) -> int:
+    return int(load_library().kda_check_seqlens(cu_seqlens, num_seqs, total_tokens, result, stream))
 
 
 def kda_status_string(status: int) -> str:
@@ -297,6 +304,23 @@ def decode_step(q, k, v, g, beta, state, out=None, stream=None):
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
     return out
+
+
+def check_seqlens(cu_seqlens, total_tokens: int) -> int:
+    """Checks packed-sequence boundaries (int32 [N + 1] on the device) for
+    cu[0] = 0, non-decreasing, cu[N] = total_tokens, on the current stream. Returns -1
+    if they hold, else the first index at which one fails (waits for the result)."""
+    import torch
+
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
+        raise ValueError("cu_seqlens must be a contiguous int32 device tensor of N + 1 >= 2 entries")
+    result = torch.empty(1, dtype=torch.int32, device=cu_seqlens.device)
+    s = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
+    st = kda_check_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, int(total_tokens), _ptr(result), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_check_seqlens")
+    return int(result.item())
 
 
 def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_state=None, d_final_state=None,

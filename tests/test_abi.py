@@ -169,3 +169,17 @@ def test_backward_stage_argument_checks(lib):
         kda.KDA_ERR_ARG
     assert kda.kda_backward_token_grad(*([p] * 6), None, *([p] * 5), dims(K=64, V=64), p, need, None) == \
         kda.KDA_ERR_UNSUPPORTED
+
+
+def test_check_seqlens_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    assert kda.kda_check_seqlens(None, 1, 16, p, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, 1, 16, None, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, 0, 16, p, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, (1 << 24) + 1, 16, p, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, 1, -1, p, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, 1, 1 << 31, p, None) == kda.KDA_ERR_ARG
+    # int32 arrays need 4-byte alignment only
+    assert kda.kda_check_seqlens(b.at(2), 1, 16, p, None) == kda.KDA_ERR_ALIGN
+    assert kda.kda_check_seqlens(p, 1, 16, b.at(6), None) == kda.KDA_ERR_ALIGN
