@@ -6,7 +6,10 @@ kernel) of the H=64, T=8192, K=V=128 bf16 workload with every input already in
 device memory. Prints one JSON line with tokens/s, the dominant kernel's roofline
 and the fp64 CPU oracle timed on the host cores as a baseline.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100]
+
+The default warm-up is long enough for the GPU clock to settle: from idle, the step
+time takes about 40 back-to-back steps to reach its steady value.
 """
 from __future__ import annotations
 
@@ -62,8 +65,8 @@ BWD_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="prefill workload (default: the H=64, T=8192 benchmark shape); see inputs.WORKLOADS")
