@@ -175,15 +175,15 @@ def decode_bench(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
+    bounds[0].record(stream)
+    for i in range(args.steps):
         step()
-        e1.record(stream)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_ms = float(np.mean([bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]))
     ms_step = wall * 1e3 / args.steps
     gate_bytes = 4 if args.gate == "scalar" else 512
     per_bh = 2 * 128 * 128 * 4 + 4 * 256 + gate_bytes + 4  # state in + out, q k v out, g, beta
@@ -248,9 +248,10 @@ def backward_bench(args, w, x):
     sp = stream.cuda_stream
     P = lambda t: t.data_ptr()  # noqa: E731
 
+    # ev: the events recorded after each of the four stages; the step's start is the
+    # previous step's last event
     def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
-        rec(0)
+        rec = (lambda i: ev[i - 1].record(stream)) if ev is not None else (lambda i: None)
         st = [kda.kda_backward_records(P(q), P(k), P(g), P(beta), cu_p, dims, P(ws), nbytes, sp)]
         rec(1)
         st.append(kda.kda_backward_states(P(v), cu_p, s0_p, dims, P(ws), nbytes, sp))
@@ -270,15 +271,18 @@ def backward_bench(args, w, x):
     if not all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv, dg, dbeta)):
         print("non-finite gradient", file=sys.stderr)
         return 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for e in evs:
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     names = ("records", "states", "state_grad", "token_grad")
-    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    marks = [[start if j == 0 else evs[j - 1][3]] + evs[j] for j in range(args.steps)]  # 5 per step
+    stage_ms = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) for i, n in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
     th = T * H
     n_s0 = 1 if s0 is not None else 0
@@ -375,29 +379,27 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def step(e0=None, e1=None, e2=None):
+    # Timed steps record an event between the two kernels (`mid`) and one at the end
+    # (`end`); a step's end event is also the next step's start, so the kernels of
+    # consecutive steps are separated by one event marker.
+    def step(mid=None, end=None):
         if args.fused:
-            if e0 is not None:
-                e0.record(stream)
             st = kda.kda_chunk_prefill_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                                              cu_p, s0_p, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
                                              ws.numel(), sp)
-            if e1 is not None:
-                e1.record(stream)
-                e2.record(stream)
+            if end is not None:
+                end.record(stream)
             if st:
                 raise kda.KdaError(st, "fused prefill")
             return
-        if e0 is not None:
-            e0.record(stream)
         st = kda.kda_intra_chunk(q.data_ptr(), k.data_ptr(), g.data_ptr(), beta.data_ptr(), cu_p, dims,
                                  ws.data_ptr(), ws.numel(), sp)
-        if e1 is not None:
-            e1.record(stream)
+        if mid is not None:
+            mid.record(stream)
         st2 = kda.kda_inter_chunk(v.data_ptr(), cu_p, s0_p, out.data_ptr(), fs.data_ptr(), dims, ws.data_ptr(),
                                   ws.numel(), sp)
-        if e2 is not None:
-            e2.record(stream)
+        if end is not None:
+            end.record(stream)
         if st or st2:
             raise kda.KdaError(st or st2, "prefill")
 
@@ -408,15 +410,21 @@ def main():
         print("non-finite output", file=sys.stderr)
         return 1
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in evs:
-        step(*e)
+    bounds[0].record(stream)
+    for i in range(args.steps):
+        step(None if args.fused else mids[i], bounds[i + 1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    inter_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    if args.fused:
+        intra_ms = float(np.mean([bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]))
+        inter_ms = 0.0
+    else:
+        intra_ms = float(np.mean([bounds[i].elapsed_time(mids[i]) for i in range(args.steps)]))
+        inter_ms = float(np.mean([mids[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]))
     ms_step = wall * 1e3 / args.steps
 
     counts = inputs.algorithmic_counts(w)
