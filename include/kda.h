@@ -39,7 +39,10 @@
  *    beta     [T, H]         fp32
  *    states   [N, H, K, V]   fp32         initial_state (read), final_state (written)
  *    cu_seqlens [N + 1]      int32        sequence boundaries; NULL means one sequence
- * Every data pointer must be 16-byte aligned.
+ * Every data pointer must be 16-byte aligned (cu_seqlens: 4-byte).
+ *
+ * Size limits (KDA_ERR_ARG beyond them, and kda_workspace_bytes returns 0):
+ * 0 <= T <= 2^31 - 1, 1 <= H <= 2^16, 1 <= N <= 2^24 and N * H < 2^25.
  */
 #ifndef KDA_H
 #define KDA_H

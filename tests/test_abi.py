@@ -67,6 +67,29 @@ def test_workspace_bytes(lib):
     assert kda.kda_workspace_bytes(dims(io=9)) == 0
 
 
+def test_size_limits(lib):
+    # the largest accepted sizes (include/kda.h): 2^31 - 1 tokens, 2^16 heads, 2^24
+    # packed sequences, N * H < 2^25
+    assert kda.kda_workspace_bytes(dims(T=(1 << 31) - 1)) > 0
+    assert kda.kda_workspace_bytes(dims(H=1 << 16)) > 0
+    assert kda.kda_workspace_bytes(dims(N=1 << 24, T=1 << 24, H=1)) > 0
+    assert kda.kda_workspace_bytes(dims(N=(1 << 24) - 1, T=1 << 24, H=2)) > 0
+    # one past each limit is rejected (no size computation overflows into a small workspace)
+    assert kda.kda_workspace_bytes(dims(T=1 << 31)) == 0
+    assert kda.kda_workspace_bytes(dims(H=(1 << 16) + 1)) == 0
+    assert kda.kda_workspace_bytes(dims(N=(1 << 24) + 1, T=1 << 25, H=1)) == 0
+    assert kda.kda_workspace_bytes(dims(N=1 << 24, T=1 << 24, H=2)) == 0       # N * H = 2^25
+    assert kda.kda_workspace_bytes(dims(N=0)) == 0
+    b = Buf()
+    p = b.at()
+    big = dims(T=1 << 31)
+    assert kda.kda_chunk_prefill(p, p, p, p, p, None, None, p, None, big, p, 1 << 60, None) == kda.KDA_ERR_ARG
+    # the workspace for the largest sizes is what the records need, not a wrapped-around value
+    per_chunk_head = 14848
+    n = kda.kda_workspace_bytes(dims(T=(1 << 31) - 1, H=64))
+    assert n >= ((1 << 31) // 16) * 64 * per_chunk_head
+
+
 class Buf:
     """Host memory standing in for device pointers: the calls below fail their
     checks before anything dereferences them."""

@@ -82,6 +82,13 @@ def test_backward_packed_ragged():
     _check(w, x, d_out, d_fs, True)
 
 
+def test_backward_recurrent_grid_larger_than_the_gpu():
+    """131 heads in two sequences: 1 056 workgroups in each reverse and forward
+    recurrence (4-deep rings, several per CU) and odd head groups in the token kernels."""
+    w, x, d_out, d_fs = _case("bwd_h131", 131, H=131, lengths=[20, 33])
+    _check(w, x, d_out, d_fs, True)
+
+
 def test_backward_scalar_gate():
     w, x, d_out, d_fs = _case("bwd_scalar", 121, H=3, T=150, gate_kind="scalar")
     _check(w, x, d_out, d_fs, False)

@@ -328,6 +328,13 @@ def test_bf16_head_counts_not_multiple_of_four(H):
     _check(w, x, False)
 
 
+def test_bf16_recurrent_grid_larger_than_the_gpu():
+    """257 heads in two sequences: 514 (sequence, head) pairs, rounded up to 520 in the
+    XCD-grouped order, i.e. 2 080 recurrent workgroups on 256 CUs with 4-deep rings."""
+    w, x = _case("bf16_h257", 257, H=257, state=True, lengths=[37, 29])
+    _check(w, x, True)
+
+
 def test_bf16_many_short_sequences():
     """150 packed sequences of 0..40 tokens (many empty or shorter than a chunk)."""
     rng = np.random.default_rng(150)
