@@ -45,7 +45,7 @@ template <typename IO, bool SCALAR_GATE>
 __global__ __launch_bounds__(kThreads) void kda_decode_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
                                                               const IO *__restrict__ v, const float *__restrict__ g,
                                                               const float *__restrict__ beta,
-                                                              float *__restrict__ state, IO *__restrict__ out, int H) {
+                                                              float *__restrict__ state, IO *__restrict__ out) {
     __shared__ float qs[KD], ks[KD], al[KD], vs[VD], dl[VD];
     __shared__ float red_k[kRowGroups][VD], red_q[kRowGroups][VD];
     __shared__ float qk_part[2];
@@ -119,7 +119,7 @@ hipError_t launch_typed(const void *q, const void *k, const void *v, const float
     auto kern = scalar_gate ? kda_decode_kernel<IO, true> : kda_decode_kernel<IO, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, static_cast<const IO *>(q),
                        static_cast<const IO *>(k), static_cast<const IO *>(v), g, beta, state,
-                       static_cast<IO *>(out), H);
+                       static_cast<IO *>(out));
     return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64) void kda_intra_f32_kernel(
         rec[F32Rec<K>::TB + idx] = TB[idx];
     }
     for (int idx = tid; idx < 16 * K; idx += 64) {
-        const int r = idx / K, ch = idx % K;
+        const int ch = idx % K;
         rec[F32Rec<K>::KD + idx] = ks[idx] * expf(G[15 * K + ch] - G[idx]);
     }
     for (int ch = tid; ch < K; ch += 64) rec[F32Rec<K>::GAM + ch] = expf(G[15 * K + ch]);
@@ -125,7 +125,7 @@ template <int K>
 __global__ __launch_bounds__(K) void kda_inter_f32_kernel(
     const float *__restrict__ v, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sT, int64_t T, int H,
-    int N, int64_t max_chunks, const float *__restrict__ records) {
+    int64_t max_chunks, const float *__restrict__ records) {
     constexpr int V = K;
     __shared__ float R[F32Rec<K>::FLOATS];
     __shared__ float D[16 * V];  // Delta of the current chunk, [token][column]
@@ -197,7 +197,7 @@ hipError_t inter_f32(const float *v, const int32_t *cu, const float *s0, float *
     const char *base = static_cast<const char *>(ws);
     hipLaunchKernelGGL(kda_inter_f32_kernel<K>, dim3(geo.N * geo.H), dim3(K), 0, stream, v, cu,
                        reinterpret_cast<const int32_t *>(base + geo.off_chunk_off), s0, out, sT, geo.T,
-                       geo.H, geo.N, geo.max_chunks, reinterpret_cast<const float *>(base + geo.off_records));
+                       geo.H, geo.max_chunks, reinterpret_cast<const float *>(base + geo.off_records));
     return hipGetLastError();
 }
 
