@@ -4,11 +4,13 @@
 // low-parallelism half of the two-kernel split (augursoft.site
 // "Kimi K3 的三個系統設計", section "為什麼 FlashKDA 選擇 16-token chunks"). The
 // state's value columns are independent (column j of S and of the output depends
-// only on column j of v and of the initial state), so a workgroup owns 32 columns
-// of one head, as two 16-column tiles, and shares one copy of each chunk's operands
-// between them. Each tile's 128 x 16 slice of S lives in MFMA accumulator registers
-// for the whole sequence, split by rows over two waves (see the compute waves below),
-// so that every SIMD of the CU runs one link of a recurrence chain.
+// only on column j of v and of the initial state), so a workgroup owns 16 NW columns
+// of one head, as NW 16-column tiles (NW = 2, or 4 when there are too few (sequence,
+// head) pairs to give every CU a 2-tile workgroup), and shares one copy of each
+// chunk's operands between them. Each tile's 128 x 16 slice of S lives in MFMA
+// accumulator registers for the whole sequence, split by rows over two waves (see the
+// compute waves below), so that every SIMD of the CU runs NW / 2 links of recurrence
+// chains.
 //
 // Per chunk, with S the state at the chunk start and V the chunk's value tile
 // (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
@@ -43,21 +45,27 @@ constexpr int VD = 128;
 constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
 
-// A workgroup has 2 kNW compute waves (kNW tiles of 16 value columns, two waves
-// each) and kNW producer waves. Producers stream each chunk into a ring slot of
-// 16 KiB with 16 wave-wide 1 KiB loads (64 lanes x 16 B), eight per producer:
+// A workgroup covers NW tiles of 16 value columns (NW = 2, or 4 when there are few
+// (sequence, head) pairs) with 2 NW compute waves (two per tile) and two producer
+// waves. Producers stream each chunk into a ring slot of 15 KiB + NW / 2 KiB with
+// wave-wide 1 KiB loads (64 lanes x 16 B):
 //   pieces 0..13  record bytes [0, 14336)          (W, Q~, K^d, T', M)
 //   piece 14      record bytes [14336, 14848) = gamma, lanes 32..63 load it again into [14848, 15360)
-//   piece 15      value tile [16 tokens][32 columns] bf16 at kVOff
-// Producer p issues record pieces 7p .. 7p + 6 and then piece 14 + p, so every load
-// of a producer has one role and each producer issues exactly kPerWave per chunk.
+//   then          value tile [16 tokens][16 NW columns] bf16 at kVOff, NW / 2 pieces
+// Producer 0 issues record pieces 0 .. 6 and gamma (kPerWave0 loads per chunk),
+// producer 1 record pieces 7 .. 13 and the value tile (per_wave1<NW>()), so every
+// load of a producer has one role and each producer issues a fixed number per chunk.
 // Only producers wait on the vector-memory counter, and they never store, so the
 // count they wait on covers their own loads alone; compute waves only read LDS,
 // compute and store.
-constexpr int kNW = 2;
-constexpr int kPerWave = 8;
-constexpr int kSlotBytes = 16384;
+constexpr int kNW = 2;  // the default tile count (and the single-kernel ablation's)
+constexpr int kPerWave0 = 8;
+template <int NW>
+constexpr int per_wave1() { return 7 + NW / 2; }
 constexpr int kVOff = 15360;
+template <int NW>
+constexpr int slot_bytes() { return kVOff + 512 * NW; }
+constexpr int kSlotBytes = slot_bytes<kNW>();  // 16 KiB
 static_assert(kRecGAM == 14336 && kRecBytesBf16 == 14848, "record layout");
 
 
@@ -65,26 +73,30 @@ static_assert(kRecGAM == 14336 && kRecBytesBf16 == 14848, "record layout");
 struct LaneOffsets {
     unsigned int rec;    // lane * 16: record pieces
     unsigned int gam;    // (lane & 31) * 16: gamma (lanes 32..63 load it twice)
-    unsigned int v;      // value tile load of this lane: token row lane / 4, 8 columns
+    unsigned int v;      // value tile load of this lane (NW = 2: token row lane / 4, 8 columns;
+                         // NW = 4: token row lane / 8, 8 columns)
+    unsigned int v2;     // NW = 4: the second value tile load (token rows 8 .. 15)
     unsigned int out;    // output: token c, columns col + 4grp .. + 3, within the chunk
     unsigned int vrow;   // one token row of v / out in bytes (H * VD * 2)
 };
 
 
-// Bytes of a chunk's rows [0, len) restricted to the workgroup's 32 columns.
+// Bytes of a chunk's rows [0, len) restricted to the workgroup's 16 NW columns.
+template <int NW>
 __device__ __forceinline__ int tile_bytes(int len, unsigned int vrow) {
-    return len > 0 ? (len - 1) * (int)vrow + kNW * 32 : 0;
+    return len > 0 ? (len - 1) * (int)vrow + NW * 32 : 0;
 }
 
 // Issue producer `producer`'s share of one chunk's loads into the ring slot at LDS byte
 // offset `slot`. `rec` (the chunk's record) and `vchunk` (the chunk's first token
 // row of v at column col0) are wave-uniform; every address is a scalar base plus a
 // per-lane offset fixed for the whole sequence.
+template <int NW>
 __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const char *rec, const char *vchunk,
                                             int len, int producer, const LaneOffsets &lo) {
     const __amdgpu_buffer_rsrc_t rr = rsrc(rec, kRecBytesBf16);
 #pragma unroll
-    for (int k = 0; k < kPerWave - 1; ++k) {
+    for (int k = 0; k < 7; ++k) {
         const int piece = 7 * producer + k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + piece * 1024), 16, lo.rec,
                                                  piece * 1024, 0, 0);
@@ -93,26 +105,35 @@ __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + kRecGAM), 16, lo.gam, kRecGAM, 0,
                                                  0);
     } else {
-        const __amdgpu_buffer_rsrc_t rv = rsrc(vchunk, tile_bytes(len, lo.vrow));
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vchunk, tile_bytes<NW>(len, lo.vrow));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(ring + slot + kVOff), 16, lo.v, 0, 0, 0);
+        if (NW == 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(ring + slot + kVOff + 1024), 16, lo.v2, 0, 0,
+                                                     0);
     }
 }
 
-// Compute waves: kNW value tiles x 2 halves of the key dimension. Compute wave
+// Compute waves: NW value tiles x 2 halves of the key dimension. Compute wave
 // (vt, kh) holds rows 64 kh .. 64 kh + 63 of tile vt's 128 x 16 state slice, i.e. the
 // four 16 x 16 accumulator tiles M = 4 kh .. 4 kh + 3. W S, Q~ S and K^d^T Delta all
 // split along those rows, so each chunk costs a wave half the MFMA and VALU work of
 // the whole slice; the two halves of a tile swap their partial W S through LDS at
 // the chunk barrier, and half 1 hands half 0 its partial Q~ S for the output.
 constexpr int kHalves = 2;
-constexpr int kComputeWaves = kNW * kHalves;
-constexpr int kWaves = kComputeWaves + kNW;  // compute waves, then producers
+constexpr int kProducers = 2;
+template <int NW>
+constexpr int compute_waves() { return NW * kHalves; }
+template <int NW>
+constexpr int waves() { return compute_waves<NW>() + kProducers; }  // compute waves, then producers
+constexpr int kComputeWaves = compute_waves<kNW>();
 
 // Exchange area after the ring: [chunk parity][tile][slot][64 lanes] f32x4 with
 // slot 0 = half 0's W S part, slot 1 = half 1's W S part minus T' V, slot 2 = half
 // 1's Q~ S part (transposed output layout).
 constexpr int kXchgSlots = 3;
-constexpr int kXchgBytes = 2 * kNW * kXchgSlots * 1024;
+template <int NW>
+constexpr int xchg_bytes() { return 2 * NW * kXchgSlots * 1024; }
+constexpr int kXchgBytes = xchg_bytes<kNW>();
 
 // One chunk's operands for one half, in registers (read from the ring slot ahead of use).
 struct HalfOps {
@@ -123,7 +144,7 @@ struct HalfOps {
     bf16x8 vv;           // [V; V] over the 32-long reduction
 };
 
-template <int KH>
+template <int KH, int NW>
 __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, int lane) {
     const int c = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -149,7 +170,7 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
     const unsigned short *vt16 = reinterpret_cast<const unsigned short *>(slot + kVOff);
     unsigned int vb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vb[i] = vt16[(4 * grp + i) * (kNW * 16) + vt * 16 + c];
+    for (int i = 0; i < 4; ++i) vb[i] = vt16[(4 * grp + i) * (NW * 16) + vt * 16 + c];
     const unsigned int v01 = vb[0] | (vb[1] << 16), v23 = vb[2] | (vb[3] << 16);
     o.vv = __builtin_bit_cast(bf16x8, make_uint4(v01, v23, v01, v23));
 }
@@ -213,7 +234,7 @@ __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &
 // Second half, after the barrier: Delta = T' V - W S from both parts (the two
 // halves form the same sum, so they hold bitwise equal Delta), the state update of
 // this wave's rows and, on half 0, the output.
-template <int KH, bool SAVE = false>
+template <int KH, bool SAVE, int NW>
 __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], const f32x4 &x, const f32x4 &y,
                                              const f32x4 &px, const f32x4 &py, char *ochunk, int len,
                                              const LaneOffsets &lo) {
@@ -230,7 +251,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
         const f32x4 yt = y + py;
         // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
         // end of a short chunk fall outside the descriptor and are dropped
-        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes(len, lo.vrow));
+        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 packed = {pack_bf16x2(yt[0], yt[1]), pack_bf16x2(yt[2], yt[3])};
         __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
@@ -241,15 +262,15 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
 // The chunk loop of compute wave (vt, KH). Barrier B_j (j = 0 .. nchunks) is passed
 // once by every wave of the workgroup: B_j (j < nchunks) publishes chunk j's ring
 // slot, and B_{j+1} also publishes the partial products of chunk j.
-template <int KH, int DEPTH, bool SAVE = false>
+template <int KH, int DEPTH, bool SAVE, int NW>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
                                              char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
                                              char *sdst0 = nullptr) {
     auto slot_of = [&](int64_t j) {
-        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
     };
     auto xchg_of = [&](int64_t j) {
-        return ring + DEPTH * kSlotBytes + (((int)(j & 1) * kNW + vt) * kXchgSlots) * 1024;
+        return ring + DEPTH * slot_bytes<NW>() + (((int)(j & 1) * NW + vt) * kXchgSlots) * 1024;
     };
     auto len_of = [&](int64_t j) {
         const int64_t rem = tok_rows - 16 * j;
@@ -265,12 +286,13 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
         wait_lgkm0();  // the partial products are in LDS before the barrier
         barrier();     // B_{j+1}
         read_partner<KH, SAVE>(xc, lane, px, py);
-        read_ops<KH>(next, slot_of(j + 1), vt, lane);
-        chunk_part_b<KH, SAVE>(cur, S, x, y, px, py, SAVE ? nullptr : o0 + (size_t)j * chunk_rows, len_of(j), lo);
+        read_ops<KH, NW>(next, slot_of(j + 1), vt, lane);
+        chunk_part_b<KH, SAVE, NW>(cur, S, x, y, px, py, SAVE ? nullptr : o0 + (size_t)j * chunk_rows, len_of(j),
+                                   lo);
     };
     HalfOps opa, opb;
     barrier();  // B_0
-    read_ops<KH>(opa, slot_of(0), vt, lane);
+    read_ops<KH, NW>(opa, slot_of(0), vt, lane);
     int64_t j = 0;
     for (; j + 2 <= nchunks; j += 2) {
         step(j, opa, opb);
@@ -283,7 +305,7 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 // loop over the LDS ring, the state slice out. Compute wave (vt, kh) owns value
 // columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63. SAVE: `states` points at
 // the sequence's first chunk in the [H][max_chunks] array of chunk start states.
-template <int DEPTH, bool SAVE = false>
+template <int DEPTH, bool SAVE, int NW>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
@@ -312,9 +334,9 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile
     char *sdst0 = SAVE ? states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16 : nullptr;
     if (kh == 0)
-        compute_wave<0, DEPTH, SAVE>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
+        compute_wave<0, DEPTH, SAVE, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
     else
-        compute_wave<1, DEPTH, SAVE>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
+        compute_wave<1, DEPTH, SAVE, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
 
     if (sT) {
 #pragma unroll
@@ -326,22 +348,23 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
 
 // SAVE: the forward recomputed for a backward pass; every chunk's start state goes to
 // `states` ([H][max_chunks] x 32 KiB fragments) and no output or final state is written.
-template <int DEPTH, bool SAVE>
-__global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
+template <int DEPTH, bool SAVE, int NW>
+__global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
     const char *__restrict__ records, char *__restrict__ states) {
+    static_assert(NW == 2 || NW == 4, "two or four value tiles per workgroup");
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
-    static_assert((DEPTH - 1) * kPerWave < 64, "a producer's loads in flight must fit the 6-bit counter");
+    static_assert((DEPTH - 1) * per_wave1<NW>() < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
     int pair, vg;
-    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    xcd_unit_split(blockIdx.x, kTiles / NW, pair, vg);
     if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
-    const int col0 = vg * kNW * 16;  // first value column of the workgroup
+    const int col0 = vg * NW * 16;  // first value column of the workgroup
     const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
 
@@ -349,13 +372,15 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     lo.vrow = (unsigned int)H * VD * 2;
     lo.rec = lane * 16;
     lo.gam = (lane & 31) * 16;
-    lo.v = (lane >> 2) * lo.vrow + (lane & 3) * 16;
+    // a value tile row is 2 NW 16-byte pieces; one wave-wide load covers 32 / NW rows
+    lo.v = (lane / (2 * NW)) * lo.vrow + (lane % (2 * NW)) * 16;
+    lo.v2 = lo.v + 8 * lo.vrow;
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
 
-    if (wid >= kComputeWaves) {
+    if (wid >= compute_waves<NW>()) {
         // ---- producer ----
-        const int p = wid - kComputeWaves;
+        const int p = wid - compute_waves<NW>();
         const char *rec0 = records + ((size_t)h * max_chunks + sc.chunk_begin) * kRecBytesBf16;  // head-major
         const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
         auto len_of = [&](int64_t j) {
@@ -363,8 +388,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
             return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
         };
         auto issue = [&](int64_t j) {
-            const unsigned int slot = (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
-            issue_chunk(ring, slot, rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows, len_of(j), p, lo);
+            const unsigned int slot =
+                (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
+            issue_chunk<NW>(ring, slot, rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows, len_of(j), p,
+                            lo);
         };
         for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
         for (int64_t j = 0; j < nchunks; ++j) {
@@ -372,7 +399,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
             const int64_t lim = j == 0 ? DEPTH - 2 : j + DEPTH - 3;
             const int64_t last = lim < nchunks - 1 ? lim : nchunks - 1;
             asm volatile("" ::: "memory");
-            wait_for_chunk<kPerWave, DEPTH>((int)(last - j));
+            if (p == 0)
+                wait_for_chunk<kPerWave0, DEPTH>((int)(last - j));
+            else
+                wait_for_chunk<per_wave1<NW>(), DEPTH>((int)(last - j));
             barrier();  // B_j
             // The slot of chunk j - 2 is free: compute waves read it after B_{j-2}
             // and consumed what they read before B_{j-1}.
@@ -383,23 +413,24 @@ __global__ __launch_bounds__(64 * kWaves) void kda_inter_bf16_kernel(
     }
 
     char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
-    compute_role<DEPTH, SAVE>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
-                              SAVE ? nullptr : sT, st);
+    compute_role<DEPTH, SAVE, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
+                                  SAVE ? nullptr : sT, st);
 }
 
-template <int DEPTH, bool SAVE>
+template <int DEPTH, bool SAVE, int NW>
 hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                   const Geometry &geo, const void *ws, hipStream_t stream) {
     const int pairs = geo.N * geo.H;
-    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / kNW);
+    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / NW);
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    const size_t lds = (size_t)DEPTH * kSlotBytes + kXchgBytes;
-    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE>;
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
+    static_assert(lds <= 160 * 1024, "LDS of one CU");
+    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, NW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kWaves), lds, stream, static_cast<const unsigned short *>(v),
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves<NW>()), lds, stream, static_cast<const unsigned short *>(v),
                        cu_seqlens, chunk_off, s0, static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N,
                        geo.max_chunks, base + geo.off_records,
                        SAVE ? const_cast<char *>(base) + geo.off_states : nullptr);
@@ -480,29 +511,38 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
         }
         return;
     }
-    compute_role<kFusedDepth>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
+    compute_role<kFusedDepth, false, kNW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
+}
+
+}  // namespace
+
+namespace {
+
+// One workgroup per 16 NW value columns of a (sequence, head): while the 2-tile
+// workgroups fit one per CU, 2 tiles with an 8-chunk ring (128 KiB + 12 KiB exchange);
+// else while 4-tile workgroups fit one per CU, 4 tiles (8 compute waves, two per
+// SIMD, sharing one record stream) with a 7-chunk ring (119 KiB + 24 KiB); beyond
+// that 2 tiles with a 4-chunk ring so that two workgroups fit on a CU.
+template <bool SAVE>
+hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
+                          const Geometry &geo, const void *ws, hipStream_t stream) {
+    constexpr int kCUs = 256;
+    const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
+    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, SAVE, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    if (pairs8 * (kTiles / 4) <= kCUs) return launch<7, SAVE, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch<4, SAVE, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 }  // namespace
 
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream) {
-    // One workgroup (4 compute + 2 producer waves) per 32 value columns of a
-    // (sequence, head). With at most one workgroup per CU the ring is 8 chunks deep
-    // (128 KiB of LDS + 12 KiB exchange); beyond that it is 4 deep so that two
-    // workgroups fit on a CU.
-    constexpr int kCUs = 256;
-    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
-    if (blocks <= kCUs) return launch<8, false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    return launch<4, false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch_by_size<false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 hipError_t launch_inter_bf16_states(const void *v, const int32_t *cu_seqlens, const float *s0,
                                     const Geometry &geo, void *ws, hipStream_t stream) {
-    constexpr int kCUs = 256;
-    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
-    if (blocks <= kCUs) return launch<8, true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
-    return launch<4, true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
+    return launch_by_size<true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
 }
 
 }  // namespace kda

@@ -82,6 +82,13 @@ def test_backward_packed_ragged():
     _check(w, x, d_out, d_fs, True)
 
 
+def test_backward_four_tile_workgroups():
+    """72 (sequence, head) pairs: the recomputed forward runs 4-tile recurrent
+    workgroups, and the chunk start states it saves feed the token gradients."""
+    w, x, d_out, d_fs = _case("bwd_nw4", 132, H=24, lengths=[20, 0, 37])
+    _check(w, x, d_out, d_fs, True)
+
+
 def test_backward_recurrent_grid_larger_than_the_gpu():
     """131 heads in two sequences: 1 056 workgroups in each reverse and forward
     recurrence (4-deep rings, several per CU) and odd head groups in the token kernels."""
