@@ -5,12 +5,11 @@
 // "Kimi K3 的三個系統設計", section "為什麼 FlashKDA 選擇 16-token chunks"). The
 // state's value columns are independent (column j of S and of the output depends
 // only on column j of v and of the initial state), so a workgroup owns 16 NW columns
-// of one head, as NW 16-column tiles (NW = 2, or 4 when there are too few (sequence,
-// head) pairs to give every CU a 2-tile workgroup), and shares one copy of each
-// chunk's operands between them. Each tile's 128 x 16 slice of S lives in MFMA
-// accumulator registers for the whole sequence, split by rows over two waves (see the
-// compute waves below), so that every SIMD of the CU runs NW / 2 links of recurrence
-// chains.
+// of one head as NW 16-column tiles, and shares one copy of each chunk's operands
+// between them. NW = 2 while each 2-tile workgroup can have a CU of its own, else 4.
+// Each tile's 128 x 16 slice of S lives in MFMA accumulator registers for the whole
+// sequence, split by rows over two waves (see the compute waves below), so that every
+// SIMD of the CU runs NW / 2 links of recurrence chains.
 //
 // Per chunk, with S the state at the chunk start and V the chunk's value tile
 // (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
@@ -45,9 +44,9 @@ constexpr int VD = 128;
 constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
 
-// A workgroup covers NW tiles of 16 value columns (NW = 2, or 4 when there are few
-// (sequence, head) pairs) with 2 NW compute waves (two per tile) and two producer
-// waves. Producers stream each chunk into a ring slot of 15 KiB + NW / 2 KiB with
+// A workgroup covers NW tiles of 16 value columns with 2 NW compute waves (two per
+// tile) and two producer waves (NW = 2, or 4 when 2-tile workgroups would outnumber
+// the CUs). Producers stream each chunk into a ring slot of 15 KiB + NW / 2 KiB with
 // wave-wide 1 KiB loads (64 lanes x 16 B):
 //   pieces 0..13  record bytes [0, 14336)          (W, Q~, K^d, T', M)
 //   piece 14      record bytes [14336, 14848) = gamma, lanes 32..63 load it again into [14848, 15360)
@@ -518,19 +517,19 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
 
 namespace {
 
-// One workgroup per 16 NW value columns of a (sequence, head): while the 2-tile
-// workgroups fit one per CU, 2 tiles with an 8-chunk ring (128 KiB + 12 KiB exchange);
-// else while 4-tile workgroups fit one per CU, 4 tiles (8 compute waves, two per
-// SIMD, sharing one record stream) with a 7-chunk ring (119 KiB + 24 KiB); beyond
-// that 2 tiles with a 4-chunk ring so that two workgroups fit on a CU.
+// One workgroup per 16 NW value columns of a (sequence, head). While 2-tile
+// workgroups fit one per CU: 2 tiles with an 8-chunk ring (128 KiB + 12 KiB
+// exchange). Beyond that: 4 tiles (8 compute waves, two per SIMD, sharing one record
+// stream) with a 7-chunk ring (119 KiB + 24 KiB), one workgroup per CU at a time.
+// Two 2-tile workgroups per CU (4-chunk rings) were slower: each streams its own copy
+// of the records.
 template <bool SAVE>
 hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                           const Geometry &geo, const void *ws, hipStream_t stream) {
     constexpr int kCUs = 256;
     const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
     if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, SAVE, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    if (pairs8 * (kTiles / 4) <= kCUs) return launch<7, SAVE, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    return launch<4, SAVE, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch<7, SAVE, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 }  // namespace

@@ -90,8 +90,9 @@ def test_backward_four_tile_workgroups():
 
 
 def test_backward_recurrent_grid_larger_than_the_gpu():
-    """131 heads in two sequences: 1 056 workgroups in each reverse and forward
-    recurrence (4-deep rings, several per CU) and odd head groups in the token kernels."""
+    """131 heads in two sequences: 528 four-tile workgroups in the recomputed forward,
+    1 056 in the reverse recurrence (4-deep rings, several per CU), and odd head groups
+    in the token kernels."""
     w, x, d_out, d_fs = _case("bwd_h131", 131, H=131, lengths=[20, 33])
     _check(w, x, d_out, d_fs, True)
 

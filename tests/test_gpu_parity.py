@@ -330,15 +330,15 @@ def test_bf16_head_counts_not_multiple_of_four(H):
 
 def test_bf16_four_tile_workgroups():
     """120 (sequence, head) pairs: too many for one 2-tile recurrent workgroup per CU,
-    few enough for 4-tile ones (8 compute waves sharing one record stream), with
-    ragged and empty packed sequences."""
+    so 4-tile ones (8 compute waves sharing one record stream), with ragged and empty
+    packed sequences."""
     w, x = _case("bf16_nw4", 124, H=24, state=True, lengths=[1, 15, 0, 33, 100])
     _check(w, x, True)
 
 
 def test_bf16_recurrent_grid_larger_than_the_gpu():
     """257 heads in two sequences: 514 (sequence, head) pairs, rounded up to 520 in the
-    XCD-grouped order, i.e. 2 080 recurrent workgroups on 256 CUs with 4-deep rings."""
+    XCD-grouped order, i.e. 1 040 four-tile recurrent workgroups, four rounds of 256 CUs."""
     w, x = _case("bf16_h257", 257, H=257, state=True, lengths=[37, 29])
     _check(w, x, True)
 
