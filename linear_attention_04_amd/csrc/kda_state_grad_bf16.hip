@@ -10,8 +10,9 @@
 // the layout the forward recomputation stores the start states in), and R after the
 // first chunk is the initial state's gradient.
 //
-// The workgroup mirrors the forward recurrent kernel: 32 value columns of one
-// (sequence, head) as two 16-column tiles, each tile's 128 x 16 slice of R held in MFMA
+// The workgroup mirrors the forward recurrent kernel: 16 NW value columns of one
+// (sequence, head) as NW 16-column tiles (NW = 2 while each 2-tile workgroup can have a
+// CU of its own, else 4), each tile's 128 x 16 slice of R held in MFMA
 // accumulators by two waves (64 key rows each), two producer waves streaming each
 // chunk's backward record and d_out tile into an LDS ring with direct buffer->LDS
 // loads, one barrier per chunk. X is a sum over all 128 keys, so the two halves of a
@@ -28,42 +29,52 @@ constexpr int KD = 128;
 constexpr int VD = 128;
 constexpr int kTiles = VD / 16;
 
-// Ring slot (16 KiB): backward record bytes [0, 12288) as 12 wave-wide 1 KiB loads,
-// gamma (512 B) loaded twice into [12288, 13312), the d_out tile [16 tokens][32
-// columns] bf16 at kDOff. Producer p issues record pieces 6p .. 6p + 5, then gamma
-// (p = 0) or the d_out tile (p = 1): kPerWave loads per chunk each.
-constexpr int kNW = 2;
-constexpr int kPerWave = 7;
-constexpr int kSlotBytes = 16384;
+// Ring slot: backward record bytes [0, 12288) as 12 wave-wide 1 KiB loads, gamma
+// (512 B) loaded twice into [12288, 13312), the d_out tile [16 tokens][16 NW columns]
+// bf16 at kDOff (NW / 2 loads). Producer 0 issues record pieces 0 .. 5 and gamma
+// (kPerWave0 loads per chunk), producer 1 record pieces 6 .. 11 and the d_out tile
+// (per_wave1<NW>()).
+constexpr int kPerWave0 = 7;
+template <int NW>
+constexpr int per_wave1() { return 6 + NW / 2; }
 constexpr int kGamOff = kBRecGAM;
 constexpr int kDOff = kBRecGAM + 1024;
-static_assert(kBRecGAM == 12288 && kBRecBytes == 12800 && kDOff + 1024 <= kSlotBytes, "backward record layout");
+template <int NW>
+constexpr int slot_bytes() { return NW == 2 ? 16384 : kDOff + 512 * NW; }
+static_assert(kBRecGAM == 12288 && kBRecBytes == 12800 && kDOff + 1024 <= slot_bytes<2>(), "backward record layout");
 
 constexpr int kHalves = 2;
-constexpr int kComputeWaves = kNW * kHalves;
-constexpr int kWaves = kComputeWaves + kNW;
+constexpr int kProducers = 2;
+template <int NW>
+constexpr int compute_waves() { return NW * kHalves; }
+template <int NW>
+constexpr int waves() { return compute_waves<NW>() + kProducers; }
 
 // Exchange area after the ring: [chunk parity][tile][half][64 lanes] f32x4, each half's
 // partial X.
-constexpr int kXchgBytes = 2 * kNW * kHalves * 1024;
+template <int NW>
+constexpr int xchg_bytes() { return 2 * NW * kHalves * 1024; }
 
 struct LaneOffsets {
     unsigned int rec;   // lane * 16
     unsigned int gam;   // (lane & 31) * 16
-    unsigned int d;     // d_out tile load of this lane: token row lane / 4, 8 columns
+    unsigned int d;     // d_out tile load of this lane (a row is 2 NW 16-byte pieces)
+    unsigned int d2;    // NW = 4: the second d_out tile load (token rows 8 .. 15)
     unsigned int vrow;  // one token row of d_out in bytes (H * VD * 2)
 };
 
+template <int NW>
 __device__ __forceinline__ int tile_bytes(int len, unsigned int vrow) {
-    return len > 0 ? (len - 1) * (int)vrow + kNW * 32 : 0;
+    return len > 0 ? (len - 1) * (int)vrow + NW * 32 : 0;
 }
 
+template <int NW>
 __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const char *brec, const char *dchunk,
                                             int len, int producer, const LaneOffsets &lo) {
     const __amdgpu_buffer_rsrc_t rr = rsrc(brec, kBRecBytes);
 #pragma unroll
-    for (int k = 0; k < kPerWave - 1; ++k) {
-        const int piece = (kPerWave - 1) * producer + k;
+    for (int k = 0; k < 6; ++k) {
+        const int piece = 6 * producer + k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + piece * 1024), 16, lo.rec,
                                                  piece * 1024, 0, 0);
     }
@@ -71,8 +82,11 @@ __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(ring + slot + kGamOff), 16, lo.gam, kBRecGAM, 0,
                                                  0);
     } else {
-        const __amdgpu_buffer_rsrc_t rd = rsrc(dchunk, tile_bytes(len, lo.vrow));
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dchunk, tile_bytes<NW>(len, lo.vrow));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(ring + slot + kDOff), 16, lo.d, 0, 0, 0);
+        if (NW == 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(ring + slot + kDOff + 1024), 16, lo.d2, 0, 0,
+                                                     0);
     }
 }
 
@@ -85,7 +99,7 @@ struct HalfOps {
     s16x4 dd;      // d_out: tokens 4grp .. + 3 of column c
 };
 
-template <int KH>
+template <int KH, int NW>
 __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, int lane) {
     const int c = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -110,7 +124,7 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
     const unsigned short *d16 = reinterpret_cast<const unsigned short *>(slot + kDOff);
     s16x4 dd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dd[i] = (short)d16[(4 * grp + i) * (kNW * 16) + vt * 16 + c];
+    for (int i = 0; i < 4; ++i) dd[i] = (short)d16[(4 * grp + i) * (NW * 16) + vt * 16 + c];
     o.dd = dd;
 }
 
@@ -161,13 +175,15 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&R)[4], co
 // forward recurrent kernel, with the chunks taken last to first (step j works on
 // chunk nchunks - 1 - j). rdst0 points at this lane's fragment of the sequence's first
 // chunk in the end-state gradient array.
-template <int KH, int DEPTH>
+template <int KH, int DEPTH, int NW>
 __device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t nchunks, int vt, int lane,
                                              char *rdst0) {
     auto slot_of = [&](int64_t j) {
-        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
+        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
     };
-    auto xchg_of = [&](int64_t j) { return ring + DEPTH * kSlotBytes + ((int)(j & 1) * kNW + vt) * kHalves * 1024; };
+    auto xchg_of = [&](int64_t j) {
+        return ring + DEPTH * slot_bytes<NW>() + ((int)(j & 1) * NW + vt) * kHalves * 1024;
+    };
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, px;
         char *xc = xchg_of(j);
@@ -175,12 +191,12 @@ __device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t 
         wait_lgkm0();  // the partial X is in LDS before the barrier
         barrier();     // B_{j+1}
         px = *reinterpret_cast<const f32x4 *>(xc + (1 - KH) * 1024 + lane * 16);
-        read_ops<KH>(next, slot_of(j + 1), vt, lane);
+        read_ops<KH, NW>(next, slot_of(j + 1), vt, lane);
         chunk_part_b<KH>(cur, R, x, px);
     };
     HalfOps opa, opb;
     barrier();  // B_0
-    read_ops<KH>(opa, slot_of(0), vt, lane);
+    read_ops<KH, NW>(opa, slot_of(0), vt, lane);
     int64_t j = 0;
     for (; j + 2 <= nchunks; j += 2) {
         step(j, opa, opb);
@@ -189,33 +205,35 @@ __device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t 
     if (j < nchunks) step(j, opa, opb);
 }
 
-template <int DEPTH>
-__global__ __launch_bounds__(64 * kWaves) void kda_state_grad_bf16_kernel(
+template <int DEPTH, int NW>
+__global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
     const unsigned short *__restrict__ d_out, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const float *__restrict__ dsT, float *__restrict__ ds0, int64_t T, int H, int N, int64_t max_chunks,
     const char *__restrict__ brecords, char *__restrict__ dstates) {
+    static_assert(NW == 2 || NW == 4, "two or four value tiles per workgroup");
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
-    static_assert((DEPTH - 1) * kPerWave < 64, "a producer's loads in flight must fit the 6-bit counter");
+    static_assert((DEPTH - 1) * per_wave1<NW>() < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
     int pair, vg;
-    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    xcd_unit_split(blockIdx.x, kTiles / NW, pair, vg);
     if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
-    const int col0 = vg * kNW * 16;
+    const int col0 = vg * NW * 16;
     const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
     const size_t head_chunk0 = (size_t)h * max_chunks + sc.chunk_begin;  // [H][max_chunks] index of chunk 0
 
-    if (wid >= kComputeWaves) {
+    if (wid >= compute_waves<NW>()) {
         // ---- producer: chunk nchunks - 1 - j into slot j % DEPTH ----
-        const int p = wid - kComputeWaves;
+        const int p = wid - compute_waves<NW>();
         LaneOffsets lo;
         lo.vrow = (unsigned int)H * VD * 2;
         lo.rec = lane * 16;
         lo.gam = (lane & 31) * 16;
-        lo.d = (lane >> 2) * lo.vrow + (lane & 3) * 16;
+        lo.d = (lane / (2 * NW)) * lo.vrow + (lane % (2 * NW)) * 16;
+        lo.d2 = lo.d + 8 * lo.vrow;
         const char *rec0 = brecords + head_chunk0 * kBRecBytes;
         const char *d0 = reinterpret_cast<const char *>(d_out) + ((size_t)sc.tok_begin * H + h) * VD * 2 +
                          (size_t)col0 * 2;
@@ -224,15 +242,19 @@ __global__ __launch_bounds__(64 * kWaves) void kda_state_grad_bf16_kernel(
             const int64_t c = nchunks - 1 - j;
             const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * c);
             const int len = rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
-            const unsigned int slot = (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * kSlotBytes);
-            issue_chunk(ring, slot, rec0 + (size_t)c * kBRecBytes, d0 + (size_t)c * chunk_rows, len, p, lo);
+            const unsigned int slot =
+                (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
+            issue_chunk<NW>(ring, slot, rec0 + (size_t)c * kBRecBytes, d0 + (size_t)c * chunk_rows, len, p, lo);
         };
         for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
         for (int64_t j = 0; j < nchunks; ++j) {
             const int64_t lim = j == 0 ? DEPTH - 2 : j + DEPTH - 3;
             const int64_t last = lim < nchunks - 1 ? lim : nchunks - 1;
             asm volatile("" ::: "memory");
-            wait_for_chunk<kPerWave, DEPTH>((int)(last - j));
+            if (p == 0)
+                wait_for_chunk<kPerWave0, DEPTH>((int)(last - j));
+            else
+                wait_for_chunk<per_wave1<NW>(), DEPTH>((int)(last - j));
             barrier();  // B_j
             // the slot of step j - 2 is free (read after B_{j-2}, consumed before B_{j-1})
             if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
@@ -259,9 +281,9 @@ __global__ __launch_bounds__(64 * kWaves) void kda_state_grad_bf16_kernel(
     char *rdst0 = dstates + head_chunk0 * kStateBytesBf16 +
                   ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16;
     if (kh == 0)
-        compute_wave<0, DEPTH>(R, ring, nchunks, vt, lane, rdst0);
+        compute_wave<0, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0);
     else
-        compute_wave<1, DEPTH>(R, ring, nchunks, vt, lane, rdst0);
+        compute_wave<1, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0);
     if (ds0) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -270,19 +292,21 @@ __global__ __launch_bounds__(64 * kWaves) void kda_state_grad_bf16_kernel(
     }
 }
 
-template <int DEPTH>
+template <int DEPTH, int NW>
 hipError_t launch(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0, const Geometry &geo,
                   void *ws, hipStream_t stream) {
     const int pairs = geo.N * geo.H;
-    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / kNW);
+    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / NW);
     char *base = static_cast<char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    const size_t lds = (size_t)DEPTH * kSlotBytes + kXchgBytes;
-    auto kern = kda_state_grad_bf16_kernel<DEPTH>;
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
+    static_assert(lds <= 160 * 1024, "LDS of one CU");
+    auto kern = kda_state_grad_bf16_kernel<DEPTH, NW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kWaves), lds, stream, static_cast<const unsigned short *>(d_out),
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves<NW>()), lds, stream,
+                       static_cast<const unsigned short *>(d_out),
                        cu_seqlens, chunk_off, dsT, ds0, geo.T, geo.H, geo.N, geo.max_chunks,
                        base + geo.off_brecords, base + geo.off_dstates);
     return hipGetLastError();
@@ -292,12 +316,13 @@ hipError_t launch(const void *d_out, const int32_t *cu_seqlens, const float *dsT
 
 hipError_t launch_state_grad_bf16(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0,
                                   const Geometry &geo, void *ws, hipStream_t stream) {
-    // as the forward recurrent kernel: an 8-deep ring with at most one workgroup per
-    // CU, else 4 deep so that two fit
+    // as the forward recurrent kernel: 2-tile workgroups while each can have a CU of
+    // its own, else 4-tile ones sharing one record stream (8-deep rings: 128 KiB + 8 KiB,
+    // 120 KiB + 16 KiB)
     constexpr int kCUs = 256;
-    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
-    if (blocks <= kCUs) return launch<8>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
-    return launch<4>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
+    const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
+    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, 2>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
+    return launch<8, 4>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
 }
 
 }  // namespace kda
