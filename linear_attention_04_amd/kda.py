@@ -63,16 +63,28 @@ class KdaError(RuntimeError):
 
 
 _lib = None
+_lib_path = None
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libkda.so; raises if it has not been built."""
-    global _lib
+    """Load libkda.so; raises if it has not been built, or if a library from another
+    path is already loaded (one process holds one copy of the kernels).
+
+    torch is imported first. The buffers and streams the library works on come from
+    torch, so the library must bind to the HIP runtime torch has loaded. Loaded before
+    torch, it would bring in the system ROCm's runtime instead, a second runtime in the
+    process, and its launches on torch's streams fail."""
+    global _lib, _lib_path
+    real = os.path.realpath(path)
     if _lib is not None:
+        if real != _lib_path:
+            raise RuntimeError(f"libkda is already loaded from {_lib_path}; cannot also load {real}")
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m linear_attention_04_amd.build`")
-    lib = ctypes.CDLL(path)
+    import torch  # noqa: F401  (its HIP runtime first)
+
+    lib = ctypes.CDLL(real)
     p, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     dims_p = ctypes.POINTER(KdaDims)
     lib.kda_workspace_bytes.argtypes = [dims_p]
@@ -106,6 +118,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_version.argtypes = []
     lib.kda_version.restype = i32
     _lib = lib
+    _lib_path = real
     return lib
 
 

@@ -206,3 +206,29 @@ def test_check_seqlens_argument_checks(lib):
     # int32 arrays need 4-byte alignment only
     assert kda.kda_check_seqlens(b.at(2), 1, 16, p, None) == kda.KDA_ERR_ALIGN
     assert kda.kda_check_seqlens(p, 1, 16, b.at(6), None) == kda.KDA_ERR_ALIGN
+
+
+def test_one_library_per_process(lib, tmp_path):
+    # the same library again is fine; a second copy from another path is refused
+    assert kda.load_library() is lib
+    assert kda.load_library(os.path.join(ROOT, "linear_attention_04_amd", "..", "linear_attention_04_amd",
+                                         "libkda.so")) is lib
+    other = tmp_path / "libkda_copy.so"
+    other.write_bytes(open(kda.LIB_PATH, "rb").read())
+    with pytest.raises(RuntimeError, match="already loaded"):
+        kda.load_library(str(other))
+
+
+def test_library_binds_to_the_hip_runtime_torch_loaded():
+    # loaded first thing in a fresh interpreter, the library must not bring a second
+    # HIP runtime into the process next to torch's
+    import ast
+    import subprocess
+    import sys
+
+    code = ("from linear_attention_04_amd import kda; kda.load_library(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    runtimes = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
