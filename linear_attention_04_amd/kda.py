@@ -66,20 +66,22 @@ _lib = None
 _lib_path = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libkda.so; raises if it has not been built, or if a library from another
-    path is already loaded (one process holds one copy of the kernels).
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libkda.so (from `path`, else the in-tree build), or return the library
+    already loaded; raises if it has not been built, or if `path` names a library other
+    than the one already loaded (one process holds one copy of the kernels).
 
     torch is imported first. The buffers and streams the library works on come from
     torch, so the library must bind to the HIP runtime torch has loaded. Loaded before
     torch, it would bring in the system ROCm's runtime instead, a second runtime in the
     process, and its launches on torch's streams fail."""
     global _lib, _lib_path
-    real = os.path.realpath(path)
     if _lib is not None:
-        if real != _lib_path:
-            raise RuntimeError(f"libkda is already loaded from {_lib_path}; cannot also load {real}")
+        if path is not None and os.path.realpath(path) != _lib_path:
+            raise RuntimeError(f"libkda is already loaded from {_lib_path}; cannot also load {path}")
         return _lib
+    path = LIB_PATH if path is None else path
+    real = os.path.realpath(path)
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m linear_attention_04_amd.build`")
     import torch  # noqa: F401  (its HIP runtime first)

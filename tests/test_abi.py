@@ -209,7 +209,8 @@ def test_check_seqlens_argument_checks(lib):
 
 
 def test_one_library_per_process(lib, tmp_path):
-    # the same library again is fine; a second copy from another path is refused
+    # without a path, or with the loaded one's, the loaded library comes back; a second
+    # copy from another path is refused
     assert kda.load_library() is lib
     assert kda.load_library(os.path.join(ROOT, "linear_attention_04_amd", "..", "linear_attention_04_amd",
                                          "libkda.so")) is lib
