@@ -97,6 +97,14 @@ def test_backward_recurrent_grid_larger_than_the_gpu():
     _check(w, x, d_out, d_fs, True)
 
 
+def test_backward_more_sequences_than_one_table_block():
+    """1 200 packed sequences of 0..12 tokens (the chunk table's carry across blocks)."""
+    rng = np.random.default_rng(1200)
+    lengths = [int(n) for n in rng.integers(0, 13, size=1200)]
+    w, x, d_out, d_fs = _case("bwd_n1200", 1201, H=2, lengths=lengths)
+    _check(w, x, d_out, d_fs, True)
+
+
 def test_backward_scalar_gate():
     w, x, d_out, d_fs = _case("bwd_scalar", 121, H=3, T=150, gate_kind="scalar")
     _check(w, x, d_out, d_fs, False)

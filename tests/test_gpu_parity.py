@@ -352,6 +352,15 @@ def test_bf16_many_short_sequences():
     _check(w, x, True)
 
 
+def test_bf16_more_sequences_than_one_table_block():
+    """1 500 packed sequences of 0..20 tokens: the chunk table scans the boundaries in
+    blocks of 1 024 sequences and carries the chunk count from one block to the next."""
+    rng = np.random.default_rng(1500)
+    lengths = [int(n) for n in rng.integers(0, 21, size=1500)]
+    w, x = _case("bf16_n1500", 1501, H=2, state=True, lengths=lengths)
+    _check(w, x, True)
+
+
 def test_prefill_graph_replay():
     """kda_chunk_prefill captured once in a HIP graph and replayed with new inputs,
     eager work and synchronisation between replays; every replay equals the eager call."""
