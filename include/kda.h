@@ -197,7 +197,9 @@ int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, cons
  *   kda_backward_state_grad: the reverse pass over the chunks from d_final_state,
  *       storing every chunk's end-state gradient and writing d_initial_state (if
  *       not NULL).
- *   kda_backward_token_grad: dq, dk, dv, dg, dbeta from the stored states. */
+ *   kda_backward_token_grad: dq, dk, dv, dg, dbeta from the stored states.
+ * The states and state_grad stages read only what the records stage wrote, not each
+ * other's results, so they may run in either order; token_grad needs all three. */
 int kda_backward_records(const void *q, const void *k, const float *g, const float *beta,
                          const int32_t *cu_seqlens, const kda_dims_t *dims, void *workspace,
                          size_t workspace_bytes, void *stream);
