@@ -146,8 +146,10 @@ def test_backward_all_sequences_empty():
     assert torch.equal(r["d_initial_state"], d_fs)
 
 
-def test_backward_stages_equal_one_call():
-    """The four stage calls on one workspace give the one-call results bitwise."""
+@pytest.mark.parametrize("reverse_first", [False, True], ids=["in_order", "reverse_pass_first"])
+def test_backward_stages_equal_one_call(reverse_first):
+    """The four stage calls on one workspace give the one-call results bitwise, also
+    with the reverse pass enqueued before the recomputed forward (they share no data)."""
     torch = gu.torch_mod()
     from linear_attention_04_amd import kda
 
@@ -162,10 +164,16 @@ def test_backward_stages_equal_one_call():
     s = torch.cuda.current_stream().cuda_stream
     assert kda.kda_backward_records(P(d["q"]), P(d["k"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]), dims,
                                     P(ws), nbytes, s) == 0
-    assert kda.kda_backward_states(P(d["v"]), P(d["cu_seqlens"]), P(d["initial_state"]), dims, P(ws), nbytes,
-                                   s) == 0
-    assert kda.kda_backward_state_grad(P(d["d_out"]), P(d["cu_seqlens"]), P(d["d_final_state"]),
-                                       P(out["d_initial_state"]), dims, P(ws), nbytes, s) == 0
+    def states():
+        assert kda.kda_backward_states(P(d["v"]), P(d["cu_seqlens"]), P(d["initial_state"]), dims, P(ws),
+                                       nbytes, s) == 0
+
+    def state_grad():
+        assert kda.kda_backward_state_grad(P(d["d_out"]), P(d["cu_seqlens"]), P(d["d_final_state"]),
+                                           P(out["d_initial_state"]), dims, P(ws), nbytes, s) == 0
+
+    for stage in ((state_grad, states) if reverse_first else (states, state_grad)):
+        stage()
     assert kda.kda_backward_token_grad(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["d_out"]),
                                        P(d["cu_seqlens"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]),
                                        P(out["dbeta"]), dims, P(ws), nbytes, s) == 0
