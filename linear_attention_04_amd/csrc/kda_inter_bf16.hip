@@ -197,8 +197,9 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
     // four consecutive value columns of one token.
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if (SAVE) {
-        *reinterpret_cast<bf16x8 *>(sdst) = sb[0];
-        *reinterpret_cast<bf16x8 *>(sdst + 1024) = sb[1];
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), reinterpret_cast<u32x4 *>(sdst));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), reinterpret_cast<u32x4 *>(sdst + 1024));
     }
     x = mfma_16x16x32(o.w[0], sb[0], zero);
     if (!SAVE) y = mfma_16x16x32(sb[0], o.qt[0], zero);

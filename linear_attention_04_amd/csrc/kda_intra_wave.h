@@ -54,6 +54,16 @@ __device__ __forceinline__ void wave_sync() {
     asm volatile("" ::: "memory");
 }
 
+// A 16-byte record store. Records are written once and read back by the recurrent
+// kernel, never by this one, so they are stored non-temporal (streamed past the
+// caches' retention policy).
+template <typename T>
+__device__ __forceinline__ void rec_store(char *p, const T &v) {
+    static_assert(sizeof(T) == 16, "16-byte stores");
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+
 __device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
     const uint2 raw = *reinterpret_cast<const uint2 *>(p);
     dst[0] = __uint_as_float(raw.x << 16);
@@ -160,7 +170,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         for (int mp = 0; mp < 4; ++mp) {
             const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + c) * kChStride + 4 * grp]);
             const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + 16 + c) * kChStride + 4 * grp]);
-            *reinterpret_cast<uint4 *>(rec + kRecKD + (mp * 64 + lane) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            rec_store(rec + kRecKD + (mp * 64 + lane) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
     }
     if (grp == 0) L.beta[c] = b;
@@ -254,8 +264,8 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     if (!head_ok) return;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        *reinterpret_cast<bf16x8 *>(rec + kRecW + (s * 64 + lane) * 16) = wv[s];
-        *reinterpret_cast<bf16x8 *>(rec + kRecQT + (s * 64 + lane) * 16) = qv[s];
+        rec_store(rec + kRecW + (s * 64 + lane) * 16, wv[s]);
+        rec_store(rec + kRecQT + (s * 64 + lane) * 16, qv[s]);
     }
     bf16x8 tbv, mmv;
 #pragma unroll

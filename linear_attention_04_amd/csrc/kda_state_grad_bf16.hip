@@ -142,8 +142,9 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&R)[4], f3
             rb[s][4 + i] = to_bf16(R[2 * s + 1][i]);
         }
     }
-    *reinterpret_cast<bf16x8 *>(rdst) = rb[0];
-    *reinterpret_cast<bf16x8 *>(rdst + 1024) = rb[1];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, rb[0]), reinterpret_cast<u32x4 *>(rdst));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, rb[1]), reinterpret_cast<u32x4 *>(rdst + 1024));
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     x = mfma_16x16x32(o.kd[0], rb[0], zero);
     x = mfma_16x16x32(o.kd[1], rb[1], x);
