@@ -102,11 +102,16 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(const IO *__restri
     __syncthreads();
 
     const float4 d4 = *reinterpret_cast<const float4 *>(&dl[4 * cg]);
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int m = 0; m < kRowsPerThread; ++m) {
         const float ki = ks[rg + kRowGroups * m];
         s[m].x += ki * d4.x; s[m].y += ki * d4.y; s[m].z += ki * d4.z; s[m].w += ki * d4.w;
-        srow[(size_t)(rg + kRowGroups * m) * (VD / 4)] = s[m];
+        // written non-temporal: the next step reads the state back from HBM anyway (the
+        // batch's states exceed the caches), and dirty lines left behind would be written
+        // back while that step streams its own reads
+        __builtin_nontemporal_store(f32x4_t{s[m].x, s[m].y, s[m].z, s[m].w},
+                                    reinterpret_cast<f32x4_t *>(srow + (size_t)(rg + kRowGroups * m) * (VD / 4)));
     }
 }
 
