@@ -73,7 +73,11 @@ __device__ __forceinline__ void store_tile(const char *lds, char *g0, size_t gst
     for (int s = 0; s < 16 / kRowsPerStore; ++s) {
         const int r = s * kRowsPerStore + lane / kLanesPerRow, j = lane % kLanesPerRow;
         const uint4 x = *reinterpret_cast<const uint4 *>(lds + tile_off<ROW>(r, 16 * j));
-        if (r < len) *reinterpret_cast<uint4 *>(g0 + (size_t)r * gstride + 16 * j) = x;
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        // non-temporal: the gradients are final outputs, not read again here
+        if (r < len)
+            __builtin_nontemporal_store(u32x4{x.x, x.y, x.z, x.w},
+                                        reinterpret_cast<u32x4 *>(g0 + (size_t)r * gstride + 16 * j));
     }
 }
 
