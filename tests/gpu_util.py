@@ -233,3 +233,12 @@ def assert_close_rel(name, got, ref, rel_l2=None, max_rel=None):
     assert rel <= rel_l2, f"{name}: rel-L2 {rel:.3e} > {rel_l2}"
     assert max_abs <= max_rel * max(scale, 1e-30), f"{name}: max|err| {max_abs:.3e} > {max_rel} * {scale:.3e}"
     return max_abs, rel
+
+
+def first_heads(x: dict, n: int) -> dict:
+    """The inputs of heads 0 .. n - 1 only (head is axis 1 of every per-head array)."""
+    out = dict(x)
+    for key in ("q", "k", "v", "g", "beta", "initial_state"):
+        if x.get(key) is not None:
+            out[key] = np.ascontiguousarray(x[key][:, :n])
+    return out

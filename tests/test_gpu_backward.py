@@ -89,6 +89,21 @@ def test_backward_four_tile_workgroups():
     _check(w, x, d_out, d_fs, True)
 
 
+def test_backward_two_and_four_tile_forms_agree_bitwise():
+    """As in the forward: the first 64 heads of a 68-head backward (4-tile workgroups in
+    both recurrences) equal a 64-head backward of the same inputs (2-tile workgroups)
+    bit for bit, every gradient."""
+    torch = gu.torch_mod()
+    w, x, d_out, d_fs = _case("bwd_forms", 169, H=68, T=150)
+    print(f"case {w.name}: H=68 vs 64 heads", flush=True)
+    got4 = gu.run_gpu_backward(gu.upload_backward(x, d_out, d_fs, False))
+    sub = gu.first_heads(x, 64)
+    got2 = gu.run_gpu_backward(gu.upload_backward(sub, np.ascontiguousarray(d_out[:, :64]),
+                                                  np.ascontiguousarray(d_fs[:, :64]), False))
+    for name in GRADS + ("d_initial_state",):
+        assert torch.equal(got4[name][:, :64], got2[name]), name
+
+
 def test_backward_recurrent_grid_larger_than_the_gpu():
     """131 heads in two sequences: 528 four-tile workgroups in the recomputed forward,
     1 056 in the reverse recurrence (4-deep rings, several per CU), and odd head groups

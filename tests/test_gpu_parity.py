@@ -336,6 +336,25 @@ def test_bf16_four_tile_workgroups():
     _check(w, x, True)
 
 
+@pytest.mark.parametrize("lengths", [None, [37, 150]])
+def test_two_and_four_tile_forms_agree_bitwise(lengths):
+    """Each head's results depend only on its own inputs, and the intra-chunk kernel
+    groups heads in fours either way. So the first 64 (sequence, head) pairs of a batch
+    past 64 pairs (4-tile recurrent workgroups) equal the same pairs run alone (2-tile
+    workgroups) bit for bit: the two forms share every product, accumulation order and
+    rounding."""
+    torch = gu.torch_mod()
+    H = 68 if lengths is None else 34
+    w, x = _case("bf16_forms", 168, H=H, T=200 if lengths is None else None, state=True, lengths=lengths)
+    packed = lengths is not None
+    n = 64 // w.num_seqs
+    print(f"case {w.name}: H={H} vs {n} heads, N={w.num_seqs}", flush=True)
+    out4, fs4 = gu.run_gpu(gu.upload(x, True, packed))
+    out2, fs2 = gu.run_gpu(gu.upload(gu.first_heads(x, n), True, packed))
+    assert torch.equal(out4[:, :n], out2)
+    assert torch.equal(fs4[:, :n], fs2)
+
+
 def test_bf16_recurrent_grid_larger_than_the_gpu():
     """257 heads in two sequences: 514 (sequence, head) pairs, rounded up to 520 in the
     XCD-grouped order, i.e. 1 040 four-tile recurrent workgroups, four rounds of 256 CUs."""
