@@ -216,6 +216,24 @@ int kda_backward_token_grad(const void *q, const void *k, const void *v, const f
                             const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* A forward for training: kda_chunk_prefill that also leaves in a backward
+ * workspace what the backward's last two stages read. It writes out and final_state
+ * (bitwise equal to kda_chunk_prefill's) and runs the records stage and a recurrence
+ * that outputs and saves every chunk's start state in the same pass. The backward of
+ * the same inputs is then kda_backward_state_grad followed by
+ * kda_backward_token_grad, with the same dims, cu_seqlens and workspace, and gives
+ * exactly kda_chunk_prefill_backward's gradients. Skipping its records and states
+ * stages is the saving.
+ * Arguments: as kda_chunk_prefill (bf16 io, K = V = 128 only), except workspace: at
+ * least kda_backward_workspace_bytes(dims) bytes, owned by the caller and left
+ * untouched by other calls until the backward stages have run on it. Status codes as
+ * kda_chunk_prefill_backward. */
+int kda_chunk_prefill_for_backward(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const int32_t *cu_seqlens,
+                                   const float *initial_state, void *out, float *final_state,
+                                   const kda_dims_t *dims, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* Checks packed-sequence boundaries on the device (the other entry points never read
  * them on the host; their kernels clamp every boundary they read, so malformed ones
  * give wrong numbers, never out-of-range accesses). Sequences are packed back to back

@@ -255,6 +255,28 @@ int kda_backward_states(const void *v, const int32_t *cu_seqlens, const float *i
                                                             static_cast<hipStream_t>(stream)));
 }
 
+int kda_chunk_prefill_for_backward(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const int32_t *cu_seqlens, const float *initial_state,
+                                   void *out, float *final_state, const kda_dims_t *dims, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    Geometry geo;
+    int st = check_backward(dims, cu_seqlens, workspace, workspace_bytes, &geo);
+    if (st == KDA_OK) st = check_data(geo, {q, k, v, g, beta, out}, {initial_state, final_state});
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cu_seqlens != nullptr) {
+        st = kda::launch_status(kda::launch_chunk_table(cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    if (geo.T > 0) {
+        st = kda::launch_status(kda::launch_intra_bf16_bwd(q, k, g, beta, cu_seqlens, geo, workspace, s));
+        if (st != KDA_OK) return st;
+    }
+    // also with T = 0: the final state of each (empty) sequence is its initial state
+    return kda::launch_status(
+        kda::launch_inter_bf16_states_out(v, cu_seqlens, initial_state, out, final_state, geo, workspace, s));
+}
+
 int kda_backward_state_grad(const void *d_out, const int32_t *cu_seqlens, const float *d_final_state,
                             float *d_initial_state, const kda_dims_t *dims, void *workspace,
                             size_t workspace_bytes, void *stream) {

@@ -177,9 +177,10 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
 
 // First half of a chunk step, before the barrier: partial W S and Q~ S over this
 // wave's rows, published to the partner; then the decay of this wave's rows.
-// SAVE (the forward recomputed for a backward pass): the chunk's start state goes
-// to `sdst` as bf16 fragments (ct, 2 KH) and (ct, 2 KH + 1), and no output is formed.
-template <int KH, bool SAVE = false>
+// SAVE (the forward for a backward pass): the chunk's start state goes to `sdst` as
+// bf16 fragments (ct, 2 KH) and (ct, 2 KH + 1). OUT: the output's partial products
+// are formed (a recomputed forward that only saves states skips them).
+template <int KH, bool SAVE = false, bool OUT = true>
 __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f32x4 &x, f32x4 &y,
                                              char *xchg, int lane, char *sdst = nullptr) {
     bf16x8 sb[2];
@@ -202,16 +203,16 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
         __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), reinterpret_cast<u32x4 *>(sdst + 1024));
     }
     x = mfma_16x16x32(o.w[0], sb[0], zero);
-    if (!SAVE) y = mfma_16x16x32(sb[0], o.qt[0], zero);
+    if (OUT) y = mfma_16x16x32(sb[0], o.qt[0], zero);
     x = mfma_16x16x32(o.w[1], sb[1], x);
-    if (!SAVE) y = mfma_16x16x32(sb[1], o.qt[1], y);
+    if (OUT) y = mfma_16x16x32(sb[1], o.qt[1], y);
     if (KH == 0) {
         *reinterpret_cast<f32x4 *>(xchg + lane * 16) = x;
-        if (!SAVE) y = mfma_16x16x32(o.vv, o.tv, y);  // + (M V)^T
+        if (OUT) y = mfma_16x16x32(o.vv, o.tv, y);  // + (M V)^T
     } else {
         x -= mfma_16x16x32(o.tv, o.vv, zero);  // - T' V
         *reinterpret_cast<f32x4 *>(xchg + 1024 + lane * 16) = x;
-        if (!SAVE) *reinterpret_cast<f32x4 *>(xchg + 2048 + lane * 16) = y;
+        if (OUT) *reinterpret_cast<f32x4 *>(xchg + 2048 + lane * 16) = y;
     }
     decay_tile<4 * KH + 0>(S[0], o.gam);
     decay_tile<4 * KH + 1>(S[1], o.gam);
@@ -221,11 +222,11 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
 
 // The partner half's contribution for chunk parity buffer `xchg`: half 0 takes
 // half 1's W S part (minus T' V) and output part; half 1 takes half 0's W S part.
-template <int KH, bool SAVE = false>
+template <int KH, bool OUT = true>
 __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &px, f32x4 &py) {
     if (KH == 0) {
         px = *reinterpret_cast<const f32x4 *>(xchg + 1024 + lane * 16);
-        if (!SAVE) py = *reinterpret_cast<const f32x4 *>(xchg + 2048 + lane * 16);
+        if (OUT) py = *reinterpret_cast<const f32x4 *>(xchg + 2048 + lane * 16);
     } else {
         px = *reinterpret_cast<const f32x4 *>(xchg + lane * 16);
     }
@@ -234,7 +235,7 @@ __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &
 // Second half, after the barrier: Delta = T' V - W S from both parts (the two
 // halves form the same sum, so they hold bitwise equal Delta), the state update of
 // this wave's rows and, on half 0, the output.
-template <int KH, bool SAVE, int NW>
+template <int KH, bool OUT, int NW>
 __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], const f32x4 &x, const f32x4 &y,
                                              const f32x4 &px, const f32x4 &py, char *ochunk, int len,
                                              const LaneOffsets &lo) {
@@ -247,7 +248,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
     const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) S[mm] = mfma_16x16x32(o.kd[mm], db, S[mm]);  // K^d^T (Delta_hi + Delta_lo)
-    if (KH == 0 && !SAVE) {
+    if (KH == 0 && OUT) {
         const f32x4 yt = y + py;
         // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
         // end of a short chunk fall outside the descriptor and are dropped
@@ -262,7 +263,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
 // The chunk loop of compute wave (vt, KH). Barrier B_j (j = 0 .. nchunks) is passed
 // once by every wave of the workgroup: B_j (j < nchunks) publishes chunk j's ring
 // slot, and B_{j+1} also publishes the partial products of chunk j.
-template <int KH, int DEPTH, bool SAVE, int NW>
+template <int KH, int DEPTH, bool SAVE, bool OUT, int NW>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
                                              char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
                                              char *sdst0 = nullptr) {
@@ -282,12 +283,12 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, y, px, py;
         char *xc = xchg_of(j);
-        chunk_part_a<KH, SAVE>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * kStateBytesBf16 : nullptr);
+        chunk_part_a<KH, SAVE, OUT>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * kStateBytesBf16 : nullptr);
         wait_lgkm0();  // the partial products are in LDS before the barrier
         barrier();     // B_{j+1}
-        read_partner<KH, SAVE>(xc, lane, px, py);
+        read_partner<KH, OUT>(xc, lane, px, py);
         read_ops<KH, NW>(next, slot_of(j + 1), vt, lane);
-        chunk_part_b<KH, SAVE, NW>(cur, S, x, y, px, py, SAVE ? nullptr : o0 + (size_t)j * chunk_rows, len_of(j),
+        chunk_part_b<KH, OUT, NW>(cur, S, x, y, px, py, OUT ? o0 + (size_t)j * chunk_rows : nullptr, len_of(j),
                                    lo);
     };
     HalfOps opa, opb;
@@ -305,7 +306,8 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 // loop over the LDS ring, the state slice out. Compute wave (vt, kh) owns value
 // columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63. SAVE: `states` points at
 // the sequence's first chunk in the [H][max_chunks] array of chunk start states.
-template <int DEPTH, bool SAVE, int NW>
+// OUT: the chunk outputs go to `out`. The final state goes to `sT` unless it is NULL.
+template <int DEPTH, bool SAVE, bool OUT, int NW>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
@@ -328,15 +330,15 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     // use sits inside the chunk loop and, since stores count on the same counter,
     // makes every chunk wait for the previous chunk's output store to complete.
     wait_vmcnt<0>();
-    char *o0 = SAVE ? nullptr : reinterpret_cast<char *>(out) + tok_bytes;  // no output when SAVE
+    char *o0 = OUT ? reinterpret_cast<char *>(out) + tok_bytes : nullptr;
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
     const int64_t tok_rows = sc.tok_end - sc.tok_begin;
     // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile
     char *sdst0 = SAVE ? states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16 : nullptr;
     if (kh == 0)
-        compute_wave<0, DEPTH, SAVE, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
+        compute_wave<0, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
     else
-        compute_wave<1, DEPTH, SAVE, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
+        compute_wave<1, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sdst0);
 
     if (sT) {
 #pragma unroll
@@ -346,9 +348,10 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     }
 }
 
-// SAVE: the forward recomputed for a backward pass; every chunk's start state goes to
-// `states` ([H][max_chunks] x 32 KiB fragments) and no output or final state is written.
-template <int DEPTH, bool SAVE, int NW>
+// SAVE: every chunk's start state goes to `states` ([H][max_chunks] x 32 KiB
+// fragments), for a backward pass. OUT: the output is written (a recomputed forward
+// that only saves states writes neither output nor final state).
+template <int DEPTH, bool SAVE, bool OUT, int NW>
 __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
@@ -413,11 +416,11 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
     }
 
     char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
-    compute_role<DEPTH, SAVE, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
-                                  SAVE ? nullptr : sT, st);
+    compute_role<DEPTH, SAVE, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
+                                       OUT ? sT : nullptr, st);
 }
 
-template <int DEPTH, bool SAVE, int NW>
+template <int DEPTH, bool SAVE, bool OUT, int NW>
 hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                   const Geometry &geo, const void *ws, hipStream_t stream) {
     const int pairs = geo.N * geo.H;
@@ -426,7 +429,7 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
-    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, NW>;
+    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
         }
         return;
     }
-    compute_role<kFusedDepth, false, kNW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
+    compute_role<kFusedDepth, false, true, kNW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT);
 }
 
 }  // namespace
@@ -524,25 +527,30 @@ namespace {
 // stream) with a 7-chunk ring (119 KiB + 24 KiB), one workgroup per CU at a time.
 // Two 2-tile workgroups per CU (4-chunk rings) were slower: each streams its own copy
 // of the records.
-template <bool SAVE>
+template <bool SAVE, bool OUT>
 hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                           const Geometry &geo, const void *ws, hipStream_t stream) {
     constexpr int kCUs = 256;
     const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
-    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, SAVE, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    return launch<7, SAVE, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, SAVE, OUT, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch<7, SAVE, OUT, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 }  // namespace
 
 hipError_t launch_inter_bf16(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
                              float *sT, const Geometry &geo, const void *ws, hipStream_t stream) {
-    return launch_by_size<false>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    return launch_by_size<false, true>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 hipError_t launch_inter_bf16_states(const void *v, const int32_t *cu_seqlens, const float *s0,
                                     const Geometry &geo, void *ws, hipStream_t stream) {
-    return launch_by_size<true>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
+    return launch_by_size<true, false>(v, cu_seqlens, s0, nullptr, nullptr, geo, ws, stream);
+}
+
+hipError_t launch_inter_bf16_states_out(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
+                                        float *sT, const Geometry &geo, void *ws, hipStream_t stream) {
+    return launch_by_size<true, true>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
 }
 
 }  // namespace kda

@@ -90,6 +90,10 @@ hipError_t launch_intra_bf16_bwd(const void *q, const void *k, const float *g, c
                                  const int32_t *cu_seqlens, const Geometry &geo, void *ws, hipStream_t stream);
 hipError_t launch_inter_bf16_states(const void *v, const int32_t *cu_seqlens, const float *s0,
                                     const Geometry &geo, void *ws, hipStream_t stream);
+// The forward with its output and final state that also saves every chunk's start
+// state for the backward (the states and the output of one recurrent pass).
+hipError_t launch_inter_bf16_states_out(const void *v, const int32_t *cu_seqlens, const float *s0, void *out,
+                                        float *sT, const Geometry &geo, void *ws, hipStream_t stream);
 hipError_t launch_state_grad_bf16(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0,
                                   const Geometry &geo, void *ws, hipStream_t stream);
 hipError_t launch_grad_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,

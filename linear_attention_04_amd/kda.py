@@ -34,6 +34,7 @@ EXPORTS = (
     "kda_decode_step",
     "kda_backward_workspace_bytes",
     "kda_chunk_prefill_backward",
+    "kda_chunk_prefill_for_backward",
     "kda_backward_records",
     "kda_backward_states",
     "kda_backward_state_grad",
@@ -105,6 +106,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_backward_workspace_bytes.restype = sz
     lib.kda_chunk_prefill_backward.argtypes = [p] * 15 + [dims_p, p, sz, p]
     lib.kda_chunk_prefill_backward.restype = i32
+    lib.kda_chunk_prefill_for_backward.argtypes = [p, p, p, p, p, p, p, p, p, dims_p, p, sz, p]
+    lib.kda_chunk_prefill_for_backward.restype = i32
     lib.kda_backward_records.argtypes = [p] * 5 + [dims_p, p, sz, p]
     lib.kda_backward_records.restype = i32
     lib.kda_backward_states.argtypes = [p] * 3 + [dims_p, p, sz, p]
@@ -169,6 +172,13 @@ def kda_chunk_prefill_backward(q, k, v, g, beta, cu_seqlens, initial_state, d_ou
                                                          d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
                                                          ctypes.byref(dims), workspace, workspace_bytes,
                                                          stream))
+
+
+def kda_chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                                   dims: KdaDims, workspace, workspace_bytes: int, stream) -> int:
+    return int(load_library().kda_chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                                             final_state, ctypes.byref(dims), workspace,
+                                                             workspace_bytes, stream))
 
 
 def kda_backward_records(q, k, g, beta, cu_seqlens, dims: KdaDims, workspace, workspace_bytes: int,
@@ -338,6 +348,41 @@ def check_seqlens(cu_seqlens, total_tokens: int) -> int:
     return int(result.item())
 
 
+def _check_d_out(v, d_out, d_final_state, dims):
+    import torch
+
+    if d_out.dtype != v.dtype or d_out.shape != v.shape or not d_out.is_cuda or not d_out.is_contiguous():
+        raise ValueError("d_out must be a contiguous device tensor like v")
+    if d_final_state is not None:
+        want = (dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v)
+        if d_final_state.dtype != torch.float32 or tuple(d_final_state.shape) != want \
+                or not d_final_state.is_cuda or not d_final_state.is_contiguous():
+            raise ValueError("d_final_state must be a contiguous fp32 device tensor [N, H, K, V]")
+
+
+def _backward_workspace(dims, device, workspace):
+    import torch
+
+    nbytes = kda_backward_workspace_bytes(dims)
+    if nbytes == 0:
+        raise KdaError(KDA_ERR_UNSUPPORTED, "kda_backward_workspace_bytes")
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the backward needs {nbytes}")
+    return workspace
+
+
+def _gradient_buffers(q, k, v, g, beta, dims, want_d_initial_state):
+    import torch
+
+    return dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                d_initial_state=torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
+                                            dtype=torch.float32, device=q.device)
+                if want_d_initial_state else None)
+
+
 def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_state=None, d_final_state=None,
                            want_d_initial_state=True, workspace=None, stream=None):
     """Gradients of chunk_prefill (bf16, K = V = 128) for L = <d_out, out> +
@@ -351,24 +396,10 @@ def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_sta
     import torch
 
     _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
-    if d_out.dtype != v.dtype or d_out.shape != v.shape or not d_out.is_cuda or not d_out.is_contiguous():
-        raise ValueError("d_out must be a contiguous device tensor like v")
     dims = make_dims(q, v, cu_seqlens, g)
-    if d_final_state is not None:
-        want = (dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v)
-        if d_final_state.dtype != torch.float32 or tuple(d_final_state.shape) != want \
-                or not d_final_state.is_cuda or not d_final_state.is_contiguous():
-            raise ValueError("d_final_state must be a contiguous fp32 device tensor [N, H, K, V]")
-    if workspace is None:
-        nbytes = kda_backward_workspace_bytes(dims)
-        if nbytes == 0:
-            raise KdaError(KDA_ERR_UNSUPPORTED, "kda_backward_workspace_bytes")
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
-               d_initial_state=torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
-                                           dtype=torch.float32, device=q.device)
-               if want_d_initial_state else None)
+    _check_d_out(v, d_out, d_final_state, dims)
+    workspace = _backward_workspace(dims, q.device, workspace)
+    out = _gradient_buffers(q, k, v, g, beta, dims, want_d_initial_state)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     st = kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                     _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(out["dq"]),
@@ -376,4 +407,55 @@ def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_sta
                                     _ptr(out["d_initial_state"]), dims, _ptr(workspace), workspace.numel(), s)
     if st != KDA_OK:
         raise KdaError(st, "kda_chunk_prefill_backward")
+    return out
+
+
+def chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None,
+                               final_state=True, workspace=None, stream=None):
+    """The forward of a training step (kda_chunk_prefill_for_backward): as
+    :func:`chunk_prefill` (bf16, K = V = 128), and the backward workspace it fills.
+    Returns (out, final_state, workspace); pass the workspace, untouched, to
+    :func:`chunk_prefill_backward_from_saved` with the same inputs."""
+    import torch
+
+    _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
+    dims = make_dims(q, v, cu_seqlens, g)
+    workspace = _backward_workspace(dims, q.device, workspace)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if final_state is True:
+        final_state = torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
+                                  dtype=torch.float32, device=q.device)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    st = kda_chunk_prefill_for_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                        _ptr(initial_state), _ptr(out), _ptr(final_state), dims,
+                                        _ptr(workspace), workspace.numel(), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_prefill_for_backward")
+    return out, final_state, workspace
+
+
+def chunk_prefill_backward_from_saved(q, k, v, g, beta, d_out, workspace, cu_seqlens=None,
+                                      d_final_state=None, want_d_initial_state=True, stream=None):
+    """The backward of a training step whose forward was
+    :func:`chunk_prefill_for_backward` on these inputs and `workspace`: only the
+    reverse pass and the token gradients run (kda_backward_state_grad, then
+    kda_backward_token_grad). Returns the gradients as :func:`chunk_prefill_backward`."""
+    import torch
+
+    _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state=None)
+    dims = make_dims(q, v, cu_seqlens, g)
+    _check_d_out(v, d_out, d_final_state, dims)
+    workspace = _backward_workspace(dims, q.device, workspace)
+    out = _gradient_buffers(q, k, v, g, beta, dims, want_d_initial_state)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    st = kda_backward_state_grad(_ptr(d_out), _ptr(cu_seqlens), _ptr(d_final_state), _ptr(out["d_initial_state"]),
+                                 dims, _ptr(workspace), workspace.numel(), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_backward_state_grad")
+    st = kda_backward_token_grad(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(d_out), _ptr(cu_seqlens),
+                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                 _ptr(out["dbeta"]), dims, _ptr(workspace), workspace.numel(), s)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_backward_token_grad")
     return out

@@ -194,6 +194,27 @@ def test_backward_stage_argument_checks(lib):
         kda.KDA_ERR_UNSUPPORTED
 
 
+def test_training_forward_argument_checks(lib):
+    b = Buf()
+    p = b.at()
+    d = dims()
+    need = kda.kda_backward_workspace_bytes(d)
+    ok = [p] * 5 + [None, None, p, None]  # q, k, v, g, beta, cu_seqlens, initial_state, out, final_state
+    # the forward's own workspace is too small: it fills the backward workspace
+    assert kda.kda_chunk_prefill_for_backward(*ok, d, p, kda.kda_workspace_bytes(d), None) == \
+        kda.KDA_ERR_WORKSPACE
+    assert kda.kda_chunk_prefill_for_backward(*ok, d, p, need - 1, None) == kda.KDA_ERR_WORKSPACE
+    bad = list(ok)
+    bad[7] = None  # out
+    assert kda.kda_chunk_prefill_for_backward(*bad, d, p, need, None) == kda.KDA_ERR_ARG
+    bad = list(ok)
+    bad[6] = b.at(4)  # initial_state misaligned
+    assert kda.kda_chunk_prefill_for_backward(*bad, d, p, need, None) == kda.KDA_ERR_ALIGN
+    assert kda.kda_chunk_prefill_for_backward(*ok, dims(N=2), p, 1 << 40, None) == kda.KDA_ERR_ARG
+    assert kda.kda_chunk_prefill_for_backward(*ok, dims(io=kda.KDA_IO_F32, K=16, V=16), p, 1 << 40, None) == \
+        kda.KDA_ERR_UNSUPPORTED
+
+
 def test_check_seqlens_argument_checks(lib):
     b = Buf()
     p = b.at()

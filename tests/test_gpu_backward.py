@@ -104,6 +104,55 @@ def test_backward_two_and_four_tile_forms_agree_bitwise():
         assert torch.equal(got4[name][:, :64], got2[name]), name
 
 
+@pytest.mark.parametrize("case", ["one_sequence", "packed", "four_tile", "scalar_gate"])
+def test_training_forward_then_saved_backward_bitwise(case):
+    """kda_chunk_prefill_for_backward gives kda_chunk_prefill's out and final state,
+    and the reverse pass and token gradients on the workspace it filled give
+    kda_chunk_prefill_backward's gradients, all bit for bit."""
+    from linear_attention_04_amd import kda
+
+    torch = gu.torch_mod()
+    spec = {"one_sequence": dict(H=5, T=150), "packed": dict(H=3, lengths=[20, 0, 37, 100]),
+            "four_tile": dict(H=24, lengths=[20, 0, 37]), "scalar_gate": dict(H=4, T=90, gate_kind="scalar")}[case]
+    w, x, d_out, d_fs = _case(f"train_{case}", 170, **spec)
+    packed = spec.get("lengths") is not None
+    print(f"case {w.name}: H={w.heads} T={w.total_tokens} N={w.num_seqs} gate={w.gate}", flush=True)
+    d = gu.upload_backward(x, d_out, d_fs, packed)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    ref_out, ref_fs = kda.chunk_prefill(*args, cu_seqlens=d["cu_seqlens"], initial_state=d["initial_state"])
+    out, fs, ws = kda.chunk_prefill_for_backward(*args, cu_seqlens=d["cu_seqlens"],
+                                                 initial_state=d["initial_state"])
+    got = kda.chunk_prefill_backward_from_saved(*args, d["d_out"], ws, cu_seqlens=d["cu_seqlens"],
+                                                d_final_state=d["d_final_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    assert torch.equal(fs, ref_fs)
+    ref = gu.run_gpu_backward(d)
+    for name in GRADS + ("d_initial_state",):
+        assert torch.equal(got[name], ref[name]), name
+
+
+def test_training_forward_and_saved_backward_without_tokens():
+    """T = 0: the training forward's final state is the initial state, and the saved
+    backward's initial-state gradient is the final-state gradient."""
+    torch = gu.torch_mod()
+    from linear_attention_04_amd import kda
+
+    H, N = 2, 3
+    s0 = torch.randn((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    d_fs = torch.randn((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    q = torch.empty((0, H, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, H, 128), dtype=torch.float32, device="cuda")
+    beta = torch.empty((0, H), dtype=torch.float32, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    out, fs, ws = kda.chunk_prefill_for_backward(q, q, q, g, beta, cu_seqlens=cu, initial_state=s0)
+    r = kda.chunk_prefill_backward_from_saved(q, q, q, g, beta, q, ws, cu_seqlens=cu, d_final_state=d_fs)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+    assert torch.equal(fs, s0)
+    assert torch.equal(r["d_initial_state"], d_fs)
+
+
 def test_backward_recurrent_grid_larger_than_the_gpu():
     """131 heads in two sequences: 528 four-tile workgroups in the recomputed forward,
     1 056 in the reverse recurrence (4-deep rings, several per CU), and odd head groups
