@@ -72,9 +72,11 @@ def parse():
                     help="prefill workload (default: the H=64, T=8192 benchmark shape); see inputs.WORKLOADS")
     ap.add_argument("--gate", choices=("channel", "scalar"), default="channel",
                     help="scalar: the same shape with one gate per token and head (Gated DeltaNet)")
-    ap.add_argument("--mode", choices=("prefill", "decode", "backward"), default="prefill",
+    ap.add_argument("--mode", choices=("prefill", "decode", "backward", "train"), default="prefill",
                     help="decode: one-token state update of --decode-batch sequences x 64 heads; "
-                         "backward: the gradients of the prefill (kda_chunk_prefill_backward, four stages)")
+                         "backward: the gradients of the prefill (kda_chunk_prefill_backward, four stages); "
+                         "train: one training step, kda_chunk_prefill_for_backward then the reverse pass and the "
+                         "token gradients on its workspace")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--fused", action="store_true",
                     help="time the single-kernel form (kda_chunk_prefill_fused) instead of the split")
@@ -332,6 +334,132 @@ def backward_bench(args, w, x):
     return 0
 
 
+def train_bench(args, w, x):
+    """One step = one training step of workload ``w``: the forward that fills the
+    backward workspace (kda_chunk_prefill_for_backward: records, then one recurrent
+    pass for the output, final state and saved chunk states), then the reverse pass
+    and the token gradients on that workspace."""
+    import numpy as np
+    import torch
+
+    from linear_attention_04_amd import inputs, kda
+
+    d_out_h, d_fs_h = inputs.output_gradients(w)
+    dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
+                         if bf else torch.from_numpy(a).to("cuda"))
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    g, beta = dev(x["g"], False), dev(x["beta"], False)
+    d_out, d_fs = dev(d_out_h, True), dev(d_fs_h, False)
+    T, H, N = w.total_tokens, w.heads, w.num_seqs
+    cu = torch.from_numpy(x["cu_seqlens"]).to("cuda") if N > 1 else None
+    s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).to("cuda")
+    cu_p = None if cu is None else cu.data_ptr()
+    s0_p = None if s0 is None else s0.data_ptr()
+    out = torch.empty_like(v)
+    fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    ds0 = torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    dims = kda.make_dims(q, v, cu, g=g)
+    nbytes = kda.kda_backward_workspace_bytes(dims)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    def step(ev=None):
+        rec = (lambda i: ev[i - 1].record(stream)) if ev is not None else (lambda i: None)
+        st = [kda.kda_chunk_prefill_for_backward(P(q), P(k), P(v), P(g), P(beta), cu_p, s0_p, P(out), P(fs), dims,
+                                                 P(ws), nbytes, sp)]
+        rec(1)
+        st.append(kda.kda_backward_state_grad(P(d_out), cu_p, P(d_fs), P(ds0), dims, P(ws), nbytes, sp))
+        rec(2)
+        st.append(kda.kda_backward_token_grad(P(q), P(k), P(v), P(g), P(beta), P(d_out), cu_p, P(dq), P(dk),
+                                              P(dv), P(dg), P(dbeta), dims, P(ws), nbytes, sp))
+        rec(3)
+        bad = [e for e in st if e]
+        if bad:
+            raise kda.KdaError(bad[0], "training step")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not all(bool(torch.isfinite(t.float()).all()) for t in (out, dq, dk, dv, dg, dbeta)):
+        print("non-finite output or gradient", file=sys.stderr)
+        return 1
+    start = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("forward", "state_grad", "token_grad")
+    marks = [[start if j == 0 else evs[j - 1][2]] + evs[j] for j in range(args.steps)]  # 4 per step
+    stage_ms = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    th = T * H
+    n_s0 = 1 if s0 is not None else 0
+    # the forward stage is two kernels: the records (as the backward's records stage)
+    # and one recurrence that reads the forward record and v and writes out and every
+    # chunk's start state
+    kern_bytes = {"forward": (BWD_BYTES_PER_TH["records"][w.gate] + 928 + 256 + 2048 + 256) * th
+                  + (2 * n_s0 + 1) * STATE_BYTES * N * H,
+                  "state_grad": BWD_BYTES_PER_TH["state_grad"][w.gate] * th + 2 * STATE_BYTES * N * H,
+                  "token_grad": BWD_BYTES_PER_TH["token_grad"][w.gate] * th}
+    dom = max(names, key=lambda n: stage_ms[n])
+    achieved = kern_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic, digest = None, None
+    if dom != "forward":  # one kernel, with its own counter summary
+        digest = source_digest(BWD_SOURCES[dom])
+        traffic = traffic_for("bwd_" + dom, digest, w.name)
+    gate_bytes = 4 if w.gate == "scalar" else 512
+    forward_compulsory = th * (3 * 256 + gate_bytes + 4 + 256) + (2 * n_s0 + 1) * STATE_BYTES * N * H
+    backward_compulsory = th * (4 * 256 + gate_bytes + 4 + 3 * 256 + gate_bytes + 4) + (n_s0 + 2) * STATE_BYTES * N * H
+    compulsory = forward_compulsory + backward_compulsory
+    path_gbs = compulsory / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": (f"KDA training step tokens/s (prefill forward and its backward), H={H} T={T} K=V=128 bf16"
+                   + (" (scalar gate)" if w.gate == "scalar" else "")),
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128, "num_seqs": N,
+                   "initial_state": s0 is not None, "chunk": 16, "gate": w.gate, "pass": "train"},
+        "path_hbm": {"algorithmic_bytes": compulsory, "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": path_gbs / HBM_PEAK_GBS},
+        "kernels_ms": stage_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": kern_bytes[dom], "source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.max_threads()
+        heads = list(range(min(H, threads)))
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"] if N > 1 else None,
+                           initial_state=x["initial_state"], heads=heads, threads=threads)
+            oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_out_h,
+                            cu_seqlens=x["cu_seqlens"] if N > 1 else None, initial_state=x["initial_state"],
+                            d_final_state=d_fs_h, heads=heads, threads=threads)
+            runs += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or runs >= 64:
+                break
+        rec["cpu_baseline"] = {
+            "value": runs * T * len(heads) / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {H} heads x {T} tokens, forward and backward, run {runs} times in "
+                      f"{dt:.2f} s, scaled to all {H} heads"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -362,6 +490,8 @@ def main():
     x = inputs.generate(w)
     if args.mode == "backward":
         return backward_bench(args, w, x)
+    if args.mode == "train":
+        return train_bench(args, w, x)
     dev = lambda a, bf: (torch.from_numpy(inputs.bf16_bits(a)).to("cuda").view(torch.bfloat16)  # noqa: E731
                          if bf else torch.from_numpy(a).to("cuda"))
     q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)

@@ -46,8 +46,9 @@ def _run_bench(*args):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("args", [(), ("--gate", "scalar"), ("--mode", "decode"), ("--mode", "backward")],
-                         ids=["prefill", "scalar_gate", "decode", "backward"])
+@pytest.mark.parametrize("args", [(), ("--gate", "scalar"), ("--mode", "decode"), ("--mode", "backward"),
+                                  ("--mode", "train")],
+                         ids=["prefill", "scalar_gate", "decode", "backward", "train"])
 def test_bench_json_line(args):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
