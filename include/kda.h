@@ -20,7 +20,9 @@
  *
  * Conventions for every entry point:
  *  - All data pointers are DEVICE pointers owned by the caller. The library
- *    allocates and frees nothing, keeps no global state and is reentrant.
+ *    allocates and frees no device memory and is reentrant; its only global state
+ *    is a per-device cache of the compute-unit and XCD counts and of the kernels'
+ *    LDS limits, filled on a device's first launch (thread-safe).
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    default stream) and the call returns without waiting. Buffers must stay
  *    alive until the stream has passed the call.
@@ -40,6 +42,17 @@
  *    states   [N, H, K, V]   fp32         initial_state (read), final_state (written)
  *    cu_seqlens [N + 1]      int32        sequence boundaries; NULL means one sequence
  * Every data pointer must be 16-byte aligned (cu_seqlens: 4-byte).
+ *
+ * Gate range. Any finite g <= 0 (a decay, of any strength) gives finite results
+ * that are exact up to the kernels' rounding. Inside each 16-token chunk the bf16
+ * kernels factor the pairwise decay exp(G_r - G_i) (G the running in-chunk sum of g)
+ * around the chunk's 8th token; a chunk in which the running gate of any channel
+ * moves more than 72 away from that token's (e.g. per-token g below -9 throughout)
+ * is computed pair by pair instead, without factoring, at a higher cost for that
+ * chunk alone. The pages say only that the gate range at 16-token chunks suits bf16
+ * (augursoft.site "Kimi K3 的三個系統設計", section "為什麼 FlashKDA 選擇
+ * 16-token chunks"). g > 0 (growth) is accepted and exact while the true states
+ * and outputs stay inside fp32's range. NaN or infinite g are not supported.
  *
  * Size limits (KDA_ERR_ARG beyond them, and kda_workspace_bytes returns 0):
  * 0 <= T <= 2^31 - 1, 1 <= H <= 2^16, 1 <= N <= 2^24 and N * H < 2^25.

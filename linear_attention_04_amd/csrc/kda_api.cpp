@@ -2,10 +2,59 @@
 // kernel launches. Nothing here touches the device before every check has passed.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "kda.h"
 #include "kda_internal.h"
 
 namespace kda {
+
+namespace {
+std::mutex g_cache_mutex;
+std::vector<std::pair<int, DeviceShape>> g_shapes;      // per device
+std::vector<std::pair<const void *, int>> g_lds_set;    // (kernel, device) pairs done
+}  // namespace
+
+hipError_t device_shape(DeviceShape *shape) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    for (const auto &it : g_shapes) {
+        if (it.first == dev) {
+            *shape = it.second;
+            return hipSuccess;
+        }
+    }
+    DeviceShape s{};
+    e = hipDeviceGetAttribute(&s.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (hipDeviceGetAttribute(&s.xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || s.xccs < 1) {
+        (void)hipGetLastError();  // an older runtime without the attribute: one die
+        s.xccs = 1;
+    }
+    if (s.cus < 1) s.cus = 1;
+    g_shapes.emplace_back(dev, s);
+    *shape = s;
+    return hipSuccess;
+}
+
+hipError_t set_dynamic_lds(const void *fn, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    for (const auto &it : g_lds_set) {
+        if (it.first == fn && it.second == dev) return hipSuccess;
+    }
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    g_lds_set.emplace_back(fn, dev);
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;

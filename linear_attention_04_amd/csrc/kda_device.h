@@ -109,15 +109,16 @@ __device__ __forceinline__ float row_inclusive_sum(float x) {
     return x;
 }
 
-// Map a linear workgroup id so that consecutive ids land on the same XCD group:
-// the dispatcher deals workgroups to the 8 XCDs round robin (id % 8), so the
-// `per_unit` workgroups that share one unit of data (e.g. the V tiles of one
-// head) are placed at ids unit_slot + 8 * k and all run behind one L2.
-__device__ __forceinline__ void xcd_unit_split(int id, int per_unit, int &unit, int &member) {
-    const int xcd = id & 7;
-    const int rest = id >> 3;
+// Map a linear workgroup id so that the workgroups of one unit of data share an XCD:
+// the dispatcher deals workgroups to the device's `xccs` XCDs round robin
+// (id % xccs), so the `per_unit` workgroups that share one unit (e.g. the value
+// tiles of one head) are placed at ids unit_slot + xccs * k and all run behind one
+// L2. The grid holds a multiple of xccs units.
+__device__ __forceinline__ void xcd_unit_split(int id, int per_unit, int xccs, int &unit, int &member) {
+    const int xcd = id % xccs;
+    const int rest = id / xccs;
     member = rest % per_unit;
-    unit = (rest / per_unit) * 8 + xcd;
+    unit = (rest / per_unit) * xccs + xcd;
 }
 
 }  // namespace kda

@@ -27,8 +27,11 @@
 // same identity product turns a token-per-lane tile into a column-per-lane tile. Every
 // layout change in this kernel is such an exact MFMA. Each state fragment is loaded
 // once; LDS holds the 16 x 16 matrices and the K+ and K^d operands.
+#include <type_traits>
+
 #include "kda_chunks.h"
 #include "kda_device.h"
+#include "kda_gate_exact.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -43,13 +46,15 @@ constexpr int kWaves = 4;
 // (dv in dt..dp during the value tiles; dg in a..dp and dq, dk in kps/kds at the end).
 struct alignas(16) GradLds {
     float a[256];    // A = diag(beta) A~, strictly lower (the forward substitution)
-    float at[256];   // A~
+    float at[256];   // A~ (strictly lower)
     float t[256];    // T = (I + A)^-1
     float tb[256];   // T' = T diag(beta)
     float dt[256];   // dT = dT' diag(beta)
     float y[256];    // Y = dT T^T
     float dat[256];  // dA~
     float dp[256];   // dP (i <= r)
+    float xdat[256]; // copies of dA~ and dP for the per-pair path of strongly decaying
+    float xdp[256];  // chunks (the originals' area gathers dg there)
     float beta[16];
     bf16x8 kps[4][64];  // K+ slabs (row layout, bf16), one per 32 keys
     bf16x8 kds[4][64];  // K^d slabs
@@ -153,6 +158,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
 
     // ================= 1. chunk factors (as the intra-chunk kernel) =================
     f32x4 pcol;  // P[4grp + i][c] (i <= r kept)
+    bool exact;  // wave-uniform: this chunk takes the per-pair gate path (kda_gate_exact.h)
     {
         float kr[32], qr[32], G[32];
 #pragma unroll
@@ -188,6 +194,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
 
         // A~ and P (two-term bf16 splits of both factors); K^d and K+ slabs
         f32x4 acc_a = zero4(), acc_p = zero4();
+        float span = 0.f;  // largest |G - G_ref| of this lane
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4], kdw[4], kpw[4];
@@ -195,6 +202,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             for (int u = 0; u < 4; ++u) {
                 const int e = 8 * s + 2 * u;
                 const float d0 = G[e] - row_bcast<7>(G[e]), d1 = G[e + 1] - row_bcast<7>(G[e + 1]);
+                span = fmaxf(span, fmaxf(fabsf(d0), fabsf(d1)));
                 const float up0 = __expf(d0), up1 = __expf(d1);
                 const float dn0 = __expf(-d0), dn1 = __expf(-d1);
                 kdw[u] = pack_bf16x2(kr[e] * (dn0 * row_bcast<15>(up0)), kr[e + 1] * (dn1 * row_bcast<15>(up1)));
@@ -218,6 +226,30 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
             acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
         }
+        exact = wave_any(span > kGateSpan);
+        if (exact) {
+            // Decay too strong for the factored form: A~ and P pair by pair, through
+            // the (not yet used) Y and dA~ areas as row-major scratch, and the K^d
+            // slabs from one exponential each.
+            exact_pair_rows(kr, qr, G, lane, L.y, L.dat);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                unsigned int kdw[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = 8 * s + 2 * u;
+                    kdw[u] = pack_bf16x2(kr[e] * __expf(row_bcast<15>(G[e]) - G[e]),
+                                         kr[e + 1] * __expf(row_bcast<15>(G[e + 1]) - G[e + 1]));
+                }
+                L.kds[s][lane] = __builtin_bit_cast(bf16x8, make_uint4(kdw[0], kdw[1], kdw[2], kdw[3]));
+            }
+            wave_sync();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc_a[i] = L.y[(4 * grp + i) * 16 + c];
+                acc_p[i] = L.dat[(4 * grp + i) * 16 + c];
+            }
+        }
         // acc_a[i] = A~[4grp + i][c], acc_p[i] = P[4grp + i][c]
         if (grp == 0) L.beta[c] = b;
         wave_sync();
@@ -225,7 +257,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * grp + i;
-            L.at[r * 16 + c] = acc_a[i];
+            // strictly lower only: the factored products above the diagonal are
+            // never used and overflow under strong decays (dA is 0 there, and 0 * inf
+            // would be NaN in dbeta's row sums)
+            L.at[r * 16 + c] = (c < r) ? acc_a[i] : 0.f;
             L.a[r * 16 + c] = (c < r) ? brow[i] * acc_a[i] : 0.f;
             pcol[i] = (c <= r) ? acc_p[i] : 0.f;
         }
@@ -347,6 +382,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             tcolT[i] = L.t[r * 16 + c];
             L.dt[r * 16 + c] = dtpa[i] * b;  // dT[r][c] = dT'[r][c] beta_c
             L.dp[r * 16 + c] = dpm[i];
+            if (exact) L.xdp[r * 16 + c] = dpm[i];
         }
         float db1 = dtpa[0] * tcolT[0] + dtpa[1] * tcolT[1] + dtpa[2] * tcolT[2] + dtpa[3] * tcolT[3];
         db1 += __shfl_xor(db1, 16, 64);
@@ -385,6 +421,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         db2 += __shfl_xor(db2, 32, 64);
         dbeta_c = db1 + db2;
         *reinterpret_cast<f32x4 *>(&L.dat[c * 16 + 4 * grp]) = dat;
+        if (exact) *reinterpret_cast<f32x4 *>(&L.xdat[c * 16 + 4 * grp]) = dat;
         wave_sync();
     }
     if (grp == 0 && row_ok) dbeta[(size_t)tok * H + h] = dbeta_c;
@@ -406,8 +443,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     char *tg = reinterpret_cast<char *>(L.a);
     char *tq = reinterpret_cast<char *>(L.kps);
     char *tk = reinterpret_cast<char *>(L.kds);
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
+    // One key tile; EXACT: the chunk's decay is too strong for the factored gate form,
+    // so the products of A~ and P with the gates are differentiated pair by pair.
+    auto key_tile = [&](int kt, auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
         const size_t kc = krow + 16 * kt + 4 * grp;  // channels 16kt + 4grp + i of token c
         f32x4 kk = zero4(), qq = zero4(), G = zero4();
         if (row_ok) {
@@ -421,37 +460,77 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
                 G = f32x4{gv.x, gv.y, gv.z, gv.w};
             }
         }
-        f32x4 up, dn, eg, ed, gam, khat, qhat, krev;
+        // ga: the gradient reaching k through A~ and P (dK^ exp(G - G_ref) + dK~ exp(G_ref - G)),
+        // gq: reaching q through P (dQ^ exp(G - G_ref)), gg: reaching G through them
+        f32x4 eg, ed, gam, ga, gq, gg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            G[i] = row_inclusive_sum(G[i]);
-            const float d = G[i] - row_bcast<7>(G[i]);
-            up[i] = __expf(d);
-            dn[i] = __expf(-d);
-            eg[i] = __expf(G[i]);
-            ed[i] = dn[i] * row_bcast<15>(up[i]);
-            gam[i] = row_bcast<15>(eg[i]);
-            khat[i] = kk[i] * up[i];
-            qhat[i] = qq[i] * up[i];
-            krev[i] = kk[i] * dn[i];
+        for (int i = 0; i < 4; ++i) G[i] = row_inclusive_sum(G[i]);
+        if (!EXACT) {
+            f32x4 up, dn, khat, qhat, krev;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = G[i] - row_bcast<7>(G[i]);
+                up[i] = __expf(d);
+                dn[i] = __expf(-d);
+                eg[i] = __expf(G[i]);
+                ed[i] = dn[i] * row_bcast<15>(up[i]);
+                gam[i] = row_bcast<15>(eg[i]);
+                khat[i] = kk[i] * up[i];
+                qhat[i] = qq[i] * up[i];
+                krev[i] = kk[i] * dn[i];
+            }
+            // channel per lane, [hi | lo] over tokens 4grp .. + 3 (identity MFMAs, exact)
+            auto chan_major = [&](f32x4 x) {
+                bf16x4 xh, xl;
+                split_bf16x4(x, xh, xl);
+                const f32x4 th = mfma_16x16x16(as_s16x4(xh), I4, zero4());
+                const f32x4 tl = mfma_16x16x16(as_s16x4(xl), I4, zero4());
+                return cat8(to_bf16x4(th), to_bf16x4(tl));
+            };
+            const bf16x8 krev_c = chan_major(krev), khat_c = chan_major(khat), qhat_c = chan_major(qhat);
+            f32x4 dkhat = mfma_16x16x32(krev_c, m_darow.hi, zero4());
+            dkhat = mfma_16x16x32(krev_c, m_darow.lo, dkhat);
+            f32x4 dkrev = mfma_16x16x32(khat_c, m_dacol.hi, zero4());
+            dkrev = mfma_16x16x32(khat_c, m_dacol.lo, dkrev);
+            dkrev = mfma_16x16x32(qhat_c, m_dpcol.hi, dkrev);
+            dkrev = mfma_16x16x32(qhat_c, m_dpcol.lo, dkrev);
+            f32x4 dqhat = mfma_16x16x32(krev_c, m_dprow.hi, zero4());
+            dqhat = mfma_16x16x32(krev_c, m_dprow.lo, dqhat);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ga[i] = dkhat[i] * up[i] + dkrev[i] * dn[i];
+                gq[i] = dqhat[i] * up[i];
+                gg[i] = dkhat[i] * khat[i] - dkrev[i] * krev[i] + dqhat[i] * qhat[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                eg[i] = __expf(G[i]);
+                ed[i] = __expf(row_bcast<15>(G[i]) - G[i]);
+                gam[i] = row_bcast<15>(eg[i]);
+                ga[i] = gq[i] = gg[i] = 0.f;
+            }
+            // A~[r][j] = sum k_r k_j w and P[r][j] = sum q_r k_j w with w = exp(G_r - G_j):
+            // this token as row r (columns j <= c) and as column j (rows r >= c)
+#pragma unroll 1
+            for (int j = 0; j < 16; ++j) {
+                const int src = (lane & 48) | j;
+                const float ar = L.xdat[c * 16 + j], pr = L.xdp[c * 16 + j];  // row c
+                const float ac = L.xdat[j * 16 + c], pc = L.xdp[j * 16 + c];  // column c
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kj = __shfl(kk[i], src, 64), qj = __shfl(qq[i], src, 64);
+                    const float gj = __shfl(G[i], src, 64);
+                    // the weights of pairs outside the triangle are never used (their
+                    // coefficients are 0) and may overflow, so they are not evaluated
+                    const float wr = j <= c ? kj * __expf(G[i] - gj) : 0.f;
+                    const float wc = j >= c ? (ac * kj + pc * qj) * __expf(gj - G[i]) : 0.f;
+                    ga[i] += ar * wr + wc;
+                    gq[i] += pr * wr;
+                    gg[i] += (ar * kk[i] + pr * qq[i]) * wr - kk[i] * wc;
+                }
+            }
         }
-        // channel per lane, [hi | lo] over tokens 4grp .. + 3 (identity MFMAs, exact)
-        auto chan_major = [&](f32x4 x) {
-            bf16x4 xh, xl;
-            split_bf16x4(x, xh, xl);
-            const f32x4 th = mfma_16x16x16(as_s16x4(xh), I4, zero4());
-            const f32x4 tl = mfma_16x16x16(as_s16x4(xl), I4, zero4());
-            return cat8(to_bf16x4(th), to_bf16x4(tl));
-        };
-        const bf16x8 krev_c = chan_major(krev), khat_c = chan_major(khat), qhat_c = chan_major(qhat);
-        f32x4 dkhat = mfma_16x16x32(krev_c, m_darow.hi, zero4());
-        dkhat = mfma_16x16x32(krev_c, m_darow.lo, dkhat);
-        f32x4 dkrev = mfma_16x16x32(khat_c, m_dacol.hi, zero4());
-        dkrev = mfma_16x16x32(khat_c, m_dacol.lo, dkrev);
-        dkrev = mfma_16x16x32(qhat_c, m_dpcol.hi, dkrev);
-        dkrev = mfma_16x16x32(qhat_c, m_dpcol.lo, dkrev);
-        f32x4 dqhat = mfma_16x16x32(krev_c, m_dprow.hi, zero4());
-        dqhat = mfma_16x16x32(krev_c, m_dprow.lo, dqhat);
 
         // dgamma for this lane's four channels: sum over the lane groups, then
         // channel 16kt + 4grp + i sits in lane 4grp + i
@@ -463,10 +542,9 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         for (int i = 0; i < 4; ++i) {
             const float dkplus = -dkp[kt][i];
             const float kd = kk[i] * ed[i];
-            dkq[i] = dkhat[i] * up[i] + dkrev[i] * dn[i] + dkplus * eg[i] + dkd[kt][i] * ed[i];
-            dqq[i] = dqhat[i] * up[i] + dqp[kt][i] * eg[i];
-            float dG = dkhat[i] * khat[i] - dkrev[i] * krev[i] + dqhat[i] * qhat[i] + dkplus * (kk[i] * eg[i]) +
-                       dqp[kt][i] * (qq[i] * eg[i]) - dkd[kt][i] * kd;
+            dkq[i] = ga[i] + dkplus * eg[i] + dkd[kt][i] * ed[i];
+            dqq[i] = gq[i] + dqp[kt][i] * eg[i];
+            float dG = gg[i] + dkplus * (kk[i] * eg[i]) + dqp[kt][i] * (qq[i] * eg[i]) - dkd[kt][i] * kd;
             const float dgc =
                 row_bcast<15>(row_inclusive_sum(dkd[kt][i] * kd)) + __shfl(dgt, 4 * grp + i, 64) * gam[i];
             if (c == len - 1) dG += dgc;
@@ -480,6 +558,13 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         } else {
             *reinterpret_cast<f32x4 *>(tg + tile_off<512>(c, 2 * cb)) = dgv;
         }
+    };
+    if (!exact) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) key_tile(kt, std::false_type{});
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) key_tile(kt, std::true_type{});
     }
     wave_sync();
     const size_t row0 = ((size_t)start * H + h) * KD;

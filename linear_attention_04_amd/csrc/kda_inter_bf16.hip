@@ -356,13 +356,13 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
-    const char *__restrict__ records, char *__restrict__ states) {
+    const char *__restrict__ records, char *__restrict__ states, int xccs) {
     static_assert(NW == 2 || NW == 4, "two or four value tiles per workgroup");
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
     static_assert((DEPTH - 1) * per_wave1<NW>() < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
     int pair, vg;
-    xcd_unit_split(blockIdx.x, kTiles / NW, pair, vg);
+    xcd_unit_split(blockIdx.x, kTiles / NW, xccs, pair, vg);
     if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -422,21 +422,21 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
 
 template <int DEPTH, bool SAVE, bool OUT, int NW>
 hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
-                  const Geometry &geo, const void *ws, hipStream_t stream) {
-    const int pairs = geo.N * geo.H;
-    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / NW);
+                  const Geometry &geo, const void *ws, const DeviceShape &dev, hipStream_t stream) {
+    const int64_t blocks = (int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / NW);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves<NW>()), lds, stream, static_cast<const unsigned short *>(v),
-                       cu_seqlens, chunk_off, s0, static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N,
-                       geo.max_chunks, base + geo.off_records,
-                       SAVE ? const_cast<char *>(base) + geo.off_states : nullptr);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * waves<NW>()), lds, stream,
+                       static_cast<const unsigned short *>(v), cu_seqlens, chunk_off, s0,
+                       static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks,
+                       base + geo.off_records, SAVE ? const_cast<char *>(base) + geo.off_states : nullptr,
+                       dev.xccs);
     return hipGetLastError();
 }
 
@@ -468,10 +468,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const unsigned short *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
-    float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks) {
+    float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks, int xccs) {
     extern __shared__ __attribute__((aligned(1024))) char ring[];  // slots, exchange, intra scratch
     int pair, vg;
-    xcd_unit_split(blockIdx.x, kTiles / kNW, pair, vg);
+    xcd_unit_split(blockIdx.x, kTiles / kNW, xccs, pair, vg);
     if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -530,10 +530,12 @@ namespace {
 template <bool SAVE, bool OUT>
 hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                           const Geometry &geo, const void *ws, hipStream_t stream) {
-    constexpr int kCUs = 256;
-    const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
-    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, SAVE, OUT, 2>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
-    return launch<7, SAVE, OUT, 4>(v, cu_seqlens, s0, out, sT, geo, ws, stream);
+    DeviceShape dev;
+    const hipError_t e = device_shape(&dev);
+    if (e != hipSuccess) return e;
+    if ((int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / 2) <= dev.cus)
+        return launch<8, SAVE, OUT, 2>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
+    return launch<7, SAVE, OUT, 4>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
 }
 
 }  // namespace
@@ -560,17 +562,20 @@ namespace kda {
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
                              const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                              const Geometry &geo, const void *ws, hipStream_t stream) {
-    const int blocks = ((geo.N * geo.H + 7) / 8) * 8 * (kTiles / kNW);
+    DeviceShape dev;
+    hipError_t e = device_shape(&dev);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / kNW);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     auto kern = geo.scalar_gate ? kda_fused_bf16_kernel<true> : kda_fused_bf16_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedLds);
+    e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)kFusedLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kFusedWaves), kFusedLds, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kFusedWaves), kFusedLds, stream,
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                        static_cast<const unsigned short *>(v), g, beta, cu_seqlens, chunk_off, s0,
-                       static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks);
+                       static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks, dev.xccs);
     return hipGetLastError();
 }
 

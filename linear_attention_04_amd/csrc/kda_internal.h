@@ -70,6 +70,18 @@ struct Geometry {
     size_t backward_bytes;
 };
 
+// The current device's compute units and XCDs, read from the runtime once per device.
+struct DeviceShape {
+    int cus;   // compute units
+    int xccs;  // XCDs (accelerator complex dies); workgroups are dealt to them round robin
+};
+hipError_t device_shape(DeviceShape *shape);
+// Raises kernel `fn`'s dynamic LDS limit to `bytes` on the current device, once per
+// (kernel, device); later calls return at once.
+hipError_t set_dynamic_lds(const void *fn, int bytes);
+// Units (e.g. (sequence, head) pairs) rounded up to a whole number per XCD.
+inline int round_to_xccs(int units, int xccs) { return (units + xccs - 1) / xccs * xccs; }
+
 // Fills g from d; returns KDA_OK or a negative status (no device access).
 int make_geometry(const kda_dims_t *d, Geometry *g);
 // make_geometry plus the backward pass's workspace areas (bf16 io only).

@@ -15,13 +15,16 @@
 // "為什麼 FlashKDA 選擇 16-token chunks": 16-token chunks and a 16 x 16 inversion).
 //
 // Numerics: gates enter A and P through exp(G - G_ref) and exp(G_ref - G) with
-// G_ref the running gate at the chunk's 8th token, so both factors stay in range
-// for any gate the chunk can hold in fp32 (|G_C| < ~80). A and P, W and M K+ use
-// two-term bf16 splits (x = x_hi + x_lo) of their factors for ~16-bit accuracy;
-// W, Q~ and K^d are rounded to bf16 once, at the end.
+// G_ref the running gate at the chunk's 8th token. Both factors stay in fp32's normal
+// range while |G - G_ref| <= kGateSpan in every channel; a chunk with a stronger decay
+// recomputes A, P and K^d pair by pair without factoring (kda_gate_exact.h), so every
+// decay gives finite, exact results. A and P, W and M K+ use two-term bf16 splits
+// (x = x_hi + x_lo) of their factors for ~16-bit accuracy; W, Q~ and K^d are rounded
+// to bf16 once, at the end.
 #pragma once
 
 #include "kda_device.h"
+#include "kda_gate_exact.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -122,6 +125,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     // K^d = k exp(G_C - G) = k dn exp(G_C - G_ref) goes to LDS right away. ----
     f32x4 acc_a = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};
+    float span = 0.f;  // largest |G - G_ref| of this lane
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         unsigned int khh[4], khl[4], kbh[4], kbl[4], qhh[4], qhl[4], kdr[4];
@@ -129,6 +133,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         for (int u = 0; u < 4; ++u) {
             const int e = 8 * s + 2 * u;
             const float d0 = G[e] - row_bcast<7>(G[e]), d1 = G[e + 1] - row_bcast<7>(G[e + 1]);
+            span = fmaxf(span, fmaxf(fabsf(d0), fabsf(d1)));
             const float up0 = __expf(d0), up1 = __expf(d1);
             const float dn0 = __expf(-d0), dn1 = __expf(-d1);
             const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);  // channel of e; e + 1 is ch + 1
@@ -161,6 +166,39 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         if (BWD && head_ok)  // K^d in the W layout: token c, channels 16j + 4grp + i
             *reinterpret_cast<uint4 *>(brec + kBRecKD + (s * 64 + lane) * 16) =
                 make_uint4(kdr[0], kdr[1], kdr[2], kdr[3]);
+    }
+
+    if (wave_any(span > kGateSpan)) {
+        // Decay too strong for the factored form: A~ and P pair by pair, through the
+        // (still unused) T' and P areas as row-major scratch, and K^d = k exp(G_C - G)
+        // in one exponential, replacing what the factored loop left.
+        exact_pair_rows(kr, qr, gr, lane, L.tb, L.p);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            unsigned int kdr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = 8 * s + 2 * u;
+                const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);
+                const __bf16 kd0 = to_bf16(kr[e] * __expf(row_bcast<15>(G[e]) - G[e]));
+                const __bf16 kd1 = to_bf16(kr[e + 1] * __expf(row_bcast<15>(G[e + 1]) - G[e + 1]));
+                L.kd[ch * kChStride + c] = kd0;
+                L.kd[(ch + 1) * kChStride + c] = kd1;
+                bf16x2 pr;
+                pr[0] = kd0;
+                pr[1] = kd1;
+                kdr[u] = __builtin_bit_cast(unsigned int, pr);
+            }
+            if (BWD && head_ok)
+                *reinterpret_cast<uint4 *>(brec + kBRecKD + (s * 64 + lane) * 16) =
+                    make_uint4(kdr[0], kdr[1], kdr[2], kdr[3]);
+        }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // into the accumulator layout: row 4grp + i, column c
+            acc_a[i] = L.tb[(4 * grp + i) * 16 + c];
+            acc_p[i] = L.p[(4 * grp + i) * 16 + c];
+        }
     }
 
     wave_sync();

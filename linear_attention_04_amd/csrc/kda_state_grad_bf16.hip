@@ -210,13 +210,13 @@ template <int DEPTH, int NW>
 __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
     const unsigned short *__restrict__ d_out, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const float *__restrict__ dsT, float *__restrict__ ds0, int64_t T, int H, int N, int64_t max_chunks,
-    const char *__restrict__ brecords, char *__restrict__ dstates) {
+    const char *__restrict__ brecords, char *__restrict__ dstates, int xccs) {
     static_assert(NW == 2 || NW == 4, "two or four value tiles per workgroup");
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
     static_assert((DEPTH - 1) * per_wave1<NW>() < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
     int pair, vg;
-    xcd_unit_split(blockIdx.x, kTiles / NW, pair, vg);
+    xcd_unit_split(blockIdx.x, kTiles / NW, xccs, pair, vg);
     if (pair >= N * H) return;  // whole workgroup
     const int n = pair / H, h = pair % H;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -295,21 +295,20 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
 
 template <int DEPTH, int NW>
 hipError_t launch(const void *d_out, const int32_t *cu_seqlens, const float *dsT, float *ds0, const Geometry &geo,
-                  void *ws, hipStream_t stream) {
-    const int pairs = geo.N * geo.H;
-    const int blocks = ((pairs + 7) / 8) * 8 * (kTiles / NW);
+                  void *ws, const DeviceShape &dev, hipStream_t stream) {
+    const int64_t blocks = (int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / NW);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     char *base = static_cast<char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
     constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     auto kern = kda_state_grad_bf16_kernel<DEPTH, NW>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves<NW>()), lds, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * waves<NW>()), lds, stream,
                        static_cast<const unsigned short *>(d_out),
                        cu_seqlens, chunk_off, dsT, ds0, geo.T, geo.H, geo.N, geo.max_chunks,
-                       base + geo.off_brecords, base + geo.off_dstates);
+                       base + geo.off_brecords, base + geo.off_dstates, dev.xccs);
     return hipGetLastError();
 }
 
@@ -320,10 +319,12 @@ hipError_t launch_state_grad_bf16(const void *d_out, const int32_t *cu_seqlens, 
     // as the forward recurrent kernel: 2-tile workgroups while each can have a CU of
     // its own, else 4-tile ones sharing one record stream (8-deep rings: 128 KiB + 8 KiB,
     // 120 KiB + 16 KiB)
-    constexpr int kCUs = 256;
-    const int pairs8 = ((geo.N * geo.H + 7) / 8) * 8;
-    if (pairs8 * (kTiles / 2) <= kCUs) return launch<8, 2>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
-    return launch<8, 4>(d_out, cu_seqlens, dsT, ds0, geo, ws, stream);
+    DeviceShape dev;
+    const hipError_t e = device_shape(&dev);
+    if (e != hipSuccess) return e;
+    if ((int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / 2) <= dev.cus)
+        return launch<8, 2>(d_out, cu_seqlens, dsT, ds0, geo, ws, dev, stream);
+    return launch<8, 4>(d_out, cu_seqlens, dsT, ds0, geo, ws, dev, stream);
 }
 
 }  // namespace kda

@@ -225,6 +225,10 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def make_dims(q, v, cu_seqlens=None, g=None) -> KdaDims:
     """Sizes from the tensors; a g of shape [T, H] selects the scalar gate."""
     import torch
@@ -263,10 +267,39 @@ def _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state):
                     ("initial_state", initial_state)):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k must be [T, H, K] and v [T, H, V]")
     T, H, K = q.shape
     if k.shape != (T, H, K) or g.shape not in ((T, H, K), (T, H)) or v.shape[:2] != (T, H) \
             or beta.shape != (T, H):
         raise ValueError("shape mismatch: q, k [T,H,K], g [T,H,K] or [T,H], v [T,H,V], beta [T,H]")
+    if cu_seqlens is not None and (cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2):
+        raise ValueError("cu_seqlens must be int32 [N + 1] with N >= 1")
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens),
+                    ("initial_state", initial_state)):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if initial_state is not None:
+        N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        if tuple(initial_state.shape) != (N, H, K, v.shape[2]):
+            raise ValueError(f"initial_state must be [N, H, K, V] = {(N, H, K, v.shape[2])}, "
+                             f"got {tuple(initial_state.shape)}")
+
+
+def _check_outputs(v, dims, out, final_state):
+    """Caller-supplied output buffers: the C ABI cannot see their sizes, so a short one
+    would be written past its end. Checked before anything is launched."""
+    import torch
+
+    if out is not None:
+        if out.dtype != v.dtype or tuple(out.shape) != tuple(v.shape) or not out.is_cuda \
+                or not out.is_contiguous() or out.device != v.device:
+            raise ValueError(f"out must be a contiguous {v.dtype} tensor {tuple(v.shape)} on {v.device}")
+    if final_state is not None and final_state is not True:
+        want = (dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v)
+        if final_state.dtype != torch.float32 or tuple(final_state.shape) != want or not final_state.is_cuda \
+                or not final_state.is_contiguous() or final_state.device != v.device:
+            raise ValueError(f"final_state must be a contiguous float32 tensor {want} on {v.device}")
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None,
@@ -284,17 +317,20 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=Non
 
     _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
     dims = make_dims(q, v, cu_seqlens, g)
+    _check_outputs(v, dims, out, final_state)
+    if workspace is None:
+        workspace = workspace_for(dims, q.device)
+    elif _nbytes(workspace) < kda_workspace_bytes(dims) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a device buffer of at least {kda_workspace_bytes(dims)} bytes")
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if final_state is True:
         final_state = torch.empty((dims.num_seqs, dims.num_heads, dims.head_k, dims.head_v),
                                   dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = workspace_for(dims, q.device)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     entry = kda_chunk_prefill_fused if fused else kda_chunk_prefill
     st = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(initial_state),
-               _ptr(out), _ptr(final_state), dims, _ptr(workspace), workspace.numel(), s)
+               _ptr(out), _ptr(final_state), dims, _ptr(workspace), _nbytes(workspace), s)
     if st != KDA_OK:
         raise KdaError(st, entry.__name__)
     return out, final_state
@@ -360,16 +396,20 @@ def _check_d_out(v, d_out, d_final_state, dims):
             raise ValueError("d_final_state must be a contiguous fp32 device tensor [N, H, K, V]")
 
 
-def _backward_workspace(dims, device, workspace):
+def _backward_workspace(dims, device, workspace, allocate=True):
+    """The caller's backward workspace, checked, or (allocate=True) a new one."""
     import torch
 
     nbytes = kda_backward_workspace_bytes(dims)
     if nbytes == 0:
         raise KdaError(KDA_ERR_UNSUPPORTED, "kda_backward_workspace_bytes")
     if workspace is None:
+        if not allocate:
+            raise ValueError("workspace is required: pass the one chunk_prefill_for_backward filled")
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if workspace.numel() < nbytes:
-        raise ValueError(f"workspace holds {workspace.numel()} bytes, the backward needs {nbytes}")
+    if _nbytes(workspace) < nbytes or not workspace.is_cuda \
+            or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous device buffer of at least {nbytes} bytes")
     return workspace
 
 
@@ -404,7 +444,7 @@ def chunk_prefill_backward(q, k, v, g, beta, d_out, cu_seqlens=None, initial_sta
     st = kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                     _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(out["dq"]),
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
-                                    _ptr(out["d_initial_state"]), dims, _ptr(workspace), workspace.numel(), s)
+                                    _ptr(out["d_initial_state"]), dims, _ptr(workspace), _nbytes(workspace), s)
     if st != KDA_OK:
         raise KdaError(st, "kda_chunk_prefill_backward")
     return out
@@ -420,6 +460,7 @@ def chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens=None, initial_state=
 
     _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state)
     dims = make_dims(q, v, cu_seqlens, g)
+    _check_outputs(v, dims, out, final_state)
     workspace = _backward_workspace(dims, q.device, workspace)
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
@@ -429,7 +470,7 @@ def chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens=None, initial_state=
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     st = kda_chunk_prefill_for_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                         _ptr(initial_state), _ptr(out), _ptr(final_state), dims,
-                                        _ptr(workspace), workspace.numel(), s)
+                                        _ptr(workspace), _nbytes(workspace), s)
     if st != KDA_OK:
         raise KdaError(st, "kda_chunk_prefill_for_backward")
     return out, final_state, workspace
@@ -446,16 +487,18 @@ def chunk_prefill_backward_from_saved(q, k, v, g, beta, d_out, workspace, cu_seq
     _check_tensors(q, k, v, g, beta, cu_seqlens, initial_state=None)
     dims = make_dims(q, v, cu_seqlens, g)
     _check_d_out(v, d_out, d_final_state, dims)
-    workspace = _backward_workspace(dims, q.device, workspace)
+    # the reverse pass reads the records and chunk states the training forward left in
+    # this workspace: a fresh buffer would hold none of them
+    workspace = _backward_workspace(dims, q.device, workspace, allocate=False)
     out = _gradient_buffers(q, k, v, g, beta, dims, want_d_initial_state)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     st = kda_backward_state_grad(_ptr(d_out), _ptr(cu_seqlens), _ptr(d_final_state), _ptr(out["d_initial_state"]),
-                                 dims, _ptr(workspace), workspace.numel(), s)
+                                 dims, _ptr(workspace), _nbytes(workspace), s)
     if st != KDA_OK:
         raise KdaError(st, "kda_backward_state_grad")
     st = kda_backward_token_grad(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(d_out), _ptr(cu_seqlens),
                                  _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
-                                 _ptr(out["dbeta"]), dims, _ptr(workspace), workspace.numel(), s)
+                                 _ptr(out["dbeta"]), dims, _ptr(workspace), _nbytes(workspace), s)
     if st != KDA_OK:
         raise KdaError(st, "kda_backward_token_grad")
     return out

@@ -242,3 +242,47 @@ def first_heads(x: dict, n: int) -> dict:
         if x.get(key) is not None:
             out[key] = np.ascontiguousarray(x[key][:, :n])
     return out
+
+
+def dg_term_scale(x: dict, ref: dict, chunk: int = 16) -> np.ndarray:
+    """Per-element magnitude of the products dg is summed from, shaped like dg.
+
+    Inside a chunk the gradient reaching the running gate is, per token and channel,
+    dG_r = q_r dq_r + k_r dk_r - 2 (K~_r dK~_r + K^d_r dK^d_r) (every gated factor
+    is q or k times an exponential of G, and dq, dk collect the same products), and
+    dg_t is the sum of dG_r over the chunk's tokens r >= t. Rounding errors of dg
+    therefore scale with these products, not with dg itself, which can be many
+    times smaller (strong decays, beta = 1 with unit keys). Returns the in-chunk
+    suffix sums of |q dq| + |k dk| (summed over the channels for a scalar gate)."""
+    q, k = np.asarray(x["q"], np.float64), np.asarray(x["k"], np.float64)
+    m = np.abs(q * ref["dq"]) + np.abs(k * ref["dk"])
+    cu = np.asarray(x["cu_seqlens"]) if x.get("cu_seqlens") is not None and len(x["cu_seqlens"]) > 2 \
+        else np.array([0, q.shape[0]])
+    out = np.zeros_like(m)
+    for n in range(len(cu) - 1):
+        for c0 in range(int(cu[n]), int(cu[n + 1]), chunk):
+            c1 = min(c0 + chunk, int(cu[n + 1]))
+            out[c0:c1] = np.cumsum(m[c0:c1][::-1], axis=0)[::-1]
+    if np.ndim(x["g"]) == 2:
+        out = out.sum(axis=-1)
+    return out
+
+
+def assert_dg_close(got, ref_dg, scale, rel_l2=None, max_rel=None):
+    """dg against the oracle, relative to |dg| plus the magnitude of the products it is
+    summed from (dg_term_scale): the same bars as the other gradients, rel-L2 and
+    max|err| against max(|dg| + scale)."""
+    rel_l2 = BWD_REL_L2 if rel_l2 is None else rel_l2
+    max_rel = BWD_MAX_REL if max_rel is None else max_rel
+    got = np.asarray(got, np.float64)
+    ref_dg = np.asarray(ref_dg, np.float64)
+    diff = got - ref_dg
+    den = float(np.linalg.norm(ref_dg) + np.linalg.norm(scale))
+    rel = float(np.linalg.norm(diff)) / max(den, 1e-300)
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    top = float(np.max(np.abs(ref_dg) + scale)) if diff.size else 0.0
+    print(f"  dg: max|err|={max_abs:.3e} (max|dg|+scale={top:.3e}) rel-L2 against |dg|+scale={rel:.3e}",
+          flush=True)
+    assert np.all(np.isfinite(got)), "dg: non-finite values"
+    assert rel <= rel_l2, f"dg: rel-L2 {rel:.3e} > {rel_l2}"
+    assert max_abs <= max_rel * max(top, 1e-30), f"dg: max|err| {max_abs:.3e} > {max_rel} * {top:.3e}"
