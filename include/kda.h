@@ -85,6 +85,7 @@ extern "C" {
 #define KDA_ERR_ALIGN (-3)       /* a data pointer is not 16-byte aligned */
 #define KDA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than kda_workspace_bytes() */
 #define KDA_ERR_LAUNCH (-5)      /* the HIP runtime reported an error at launch */
+#define KDA_ERR_CAPACITY (-6)    /* larger than kda_chunk_prefill_noalloc's fixed scratch buffer */
 
 /* Problem sizes. Supported: io bf16 with K = V = 128; io fp32 with K = V in {16, 32, 64, 128}. */
 typedef struct kda_dims {
@@ -261,6 +262,33 @@ int kda_chunk_prefill_for_backward(const void *q, const void *k, const void *v, 
  * total_tokens outside [0, 2^31 - 1]; KDA_ERR_ALIGN for misaligned pointers. */
 int kda_check_seqlens(const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t *result,
                       void *stream);
+
+/* Bytes of the device buffer kda_chunk_prefill_noalloc works in (64 MiB). The library
+ * holds one on every device it runs on, from the first launch there until the process
+ * ends. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kda_chunk_prefill without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation). Arguments, layouts and results as kda_chunk_prefill, bitwise. The
+ * workspace is a fixed buffer of KDA_NOALLOC_SCRATCH_BYTES that the library keeps on
+ * each device; this call allocates and frees nothing.
+ *  - When kda_workspace_bytes(dims) fits the buffer, the call is one
+ *    kda_chunk_prefill.
+ *  - A single sequence (num_seqs = 1) that does not fit runs in segments of whole
+ *    16-token chunks, carrying the fp32 state between them inside the buffer. With
+ *    num_seqs = 1 the boundaries are taken as [0, T) and cu_seqlens is not read.
+ *    Each segment is two launches.
+ *  - A packed batch that does not fit, or a head count whose two fp32 state carriers
+ *    and one chunk's records do not fit, returns KDA_ERR_CAPACITY before anything is
+ *    enqueued.
+ * Every call on a device uses that device's one buffer and leaves its contents behind
+ * (nothing in it needs to start at zero). Calls that overlap on one device, from
+ * several streams or host threads, race on it and give wrong results: serialise them. */
+int kda_chunk_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const int32_t *cu_seqlens,
+                              const float *initial_state, void *out, float *final_state,
+                              const kda_dims_t *dims, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);

@@ -25,6 +25,7 @@ SOURCES = [
     "kda_decode.hip",
     "kda_state_grad_bf16.hip",
     "kda_grad_bf16.hip",
+    "kda_noalloc.hip",
 ]
 
 ARCH = "gfx950"

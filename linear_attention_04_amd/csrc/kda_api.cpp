@@ -391,6 +391,7 @@ const char *kda_status_string(int status) {
     case KDA_ERR_ALIGN: return "a data pointer is misaligned (16 bytes; 4 for int32 arrays)";
     case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_workspace_bytes()";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_CAPACITY: return "problem larger than kda_chunk_prefill_noalloc's fixed scratch buffer";
     default: return "unknown status";
     }
 }

@@ -24,6 +24,8 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_ALIGN = -3
 KDA_ERR_WORKSPACE = -4
 KDA_ERR_LAUNCH = -5
+KDA_ERR_CAPACITY = -6
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "kda_workspace_bytes",
@@ -40,6 +42,7 @@ EXPORTS = (
     "kda_backward_state_grad",
     "kda_backward_token_grad",
     "kda_check_seqlens",
+    "kda_chunk_prefill_noalloc",
     "kda_status_string",
     "kda_version",
 )
@@ -116,6 +119,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_backward_state_grad.restype = i32
     lib.kda_backward_token_grad.argtypes = [p] * 12 + [dims_p, p, sz, p]
     lib.kda_backward_token_grad.restype = i32
+    lib.kda_chunk_prefill_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, dims_p, p]
+    lib.kda_chunk_prefill_noalloc.restype = i32
     lib.kda_check_seqlens.argtypes = [p, ctypes.c_int32, ctypes.c_int64, p, p]
     lib.kda_check_seqlens.restype = i32
     lib.kda_status_string.argtypes = [i32]
@@ -203,6 +208,12 @@ def kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg,
                             workspace, workspace_bytes: int, stream) -> int:
     return int(load_library().kda_backward_token_grad(q, k, v, g, beta, d_out, cu_seqlens, dq, dk, dv, dg, dbeta,
                                                       ctypes.byref(dims), workspace, workspace_bytes, stream))
+
+
+def kda_chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, dims: KdaDims,
+                              stream) -> int:
+    return int(load_library().kda_chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                                        final_state, ctypes.byref(dims), stream))
 
 
 def kda_check_seqlens(cu_seqlens, num_seqs: int, total_tokens: int, result, stream) -> int:

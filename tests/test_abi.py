@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function(lib):
 def test_version_and_status_strings(lib):
     assert kda.kda_version() >= 200
     for st in (kda.KDA_OK, kda.KDA_ERR_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_ALIGN,
-               kda.KDA_ERR_WORKSPACE, kda.KDA_ERR_LAUNCH):
+               kda.KDA_ERR_WORKSPACE, kda.KDA_ERR_LAUNCH, kda.KDA_ERR_CAPACITY):
         s = kda.kda_status_string(st)
         assert isinstance(s, str) and s
     assert kda.kda_status_string(12345)
@@ -254,3 +254,22 @@ def test_library_binds_to_the_hip_runtime_torch_loaded():
     assert r.returncode == 0, r.stderr[-2000:]
     runtimes = ast.literal_eval(r.stdout.strip().splitlines()[-1])
     assert len(runtimes) == 1, runtimes
+
+
+def test_noalloc_argument_checks(lib):
+    """kda_chunk_prefill_noalloc rejects bad arguments and problems beyond its fixed
+    buffer before it looks the buffer up or enqueues anything."""
+    f = kda.kda_chunk_prefill_noalloc
+    fake = 1 << 20  # an aligned non-NULL address that is never dereferenced
+    ptrs = [fake] * 5
+    assert f(*ptrs, None, None, fake, None, dims(H=0), None) == kda.KDA_ERR_ARG
+    assert f(*ptrs, None, None, fake, None, dims(K=64, V=64), None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*ptrs, None, None, fake, None, dims(N=2), None) == kda.KDA_ERR_ARG  # N > 1 needs cu_seqlens
+    assert f(None, *ptrs[1:], None, None, fake, None, dims(), None) == kda.KDA_ERR_ARG
+    assert f(fake + 8, *ptrs[1:], None, None, fake, None, dims(), None) == kda.KDA_ERR_ALIGN
+    # a packed batch whose workspace exceeds the buffer (2 x 8192 tokens x 64 heads)
+    big = dims(T=16384, H=64, N=2)
+    assert kda.kda_workspace_bytes(big) > kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert f(*ptrs, fake, None, fake, None, big, None) == kda.KDA_ERR_CAPACITY
+    # one sequence with so many heads that two fp32 state carriers fill the buffer
+    assert f(*ptrs, None, None, fake, None, dims(T=64, H=4096), None) == kda.KDA_ERR_CAPACITY
