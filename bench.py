@@ -14,7 +14,6 @@ time takes about 40 back-to-back steps to reach its steady value.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -53,12 +52,6 @@ BWD_BYTES_PER_TH = {
     "states": {"channel": 928 + 256 + 2048, "scalar": 928 + 256 + 2048},
     "state_grad": {"channel": 800 + 256 + 2048, "scalar": 800 + 256 + 2048},
     "token_grad": {"channel": 1024 + 512 + 4 + 4096 + 768 + 512 + 4, "scalar": 1024 + 4 + 4 + 4096 + 768 + 4 + 4},
-}
-BWD_SOURCES = {
-    "records": ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_device.h", "kda_chunks.h"],
-    "states": ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
-    "state_grad": ["kda_state_grad_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
-    "token_grad": ["kda_grad_bf16.hip", "kda_device.h", "kda_chunks.h"],
 }
 
 
@@ -99,25 +92,40 @@ def copy_calibration():
     return 0
 
 
-def source_digest(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "linear_attention_04_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def source_digest(tag: str) -> str:
+    from linear_attention_04_amd import rocprof_report
+
+    return rocprof_report.source_digest(rocprof_report.KERNEL_SOURCES[tag])
 
 
-def traffic_for(kernel: str, digest: str, workload: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken on
-    the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+def profile_for(tag: str, workload: str):
+    """The committed counter summary of kernel `tag` on `workload`
+    (profiles/traffic_<tag>_<workload>.json, written by linear_attention_04_amd.rocprof_report),
+    if it was taken on the kernel's current sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{tag}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("source_digest") != digest:
+    if doc.get("source_digest") != source_digest(tag):
         return None
-    return doc.get("hbm_bytes_per_launch")
+    return doc
+
+
+def traffic_for(tag: str, workload: str):
+    """Measured HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE), or None."""
+    doc = profile_for(tag, workload)
+    return None if doc is None else doc.get("hbm_bytes_per_launch")
+
+
+def mfma_busy_for(tag: str, workload: str):
+    """Share of SIMD cycles the matrix cores were busy in kernel `tag`
+    (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8), or None."""
+    doc = profile_for(tag, workload)
+    sq = None if doc is None else doc.get("sq_counters_per_dispatch")
+    if not sq or not sq.get("GRBM_GUI_ACTIVE"):
+        return None
+    return sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * sq["GRBM_GUI_ACTIVE"] / 8)
 
 
 def cpu_baseline(x, w, min_seconds: float = 10.0, max_repeats: int = 64):
@@ -201,8 +209,8 @@ def decode_bench(args):
         "kernels_ms": {"decode": kern_ms},
         "roofline": {"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for("decode", source_digest(["kda_decode.hip", "kda_device.h"]), w.name),
-                     "algorithmic_bytes": alg, "source_digest": source_digest(["kda_decode.hip", "kda_device.h"])},
+                     "traffic": traffic_for("decode", w.name), "algorithmic_bytes": alg,
+                     "source_digest": source_digest("decode")},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -292,7 +300,7 @@ def backward_bench(args, w, x):
     kern_bytes = {n: BWD_BYTES_PER_TH[n][w.gate] * th + extra_states[n] * STATE_BYTES * N * H for n in names}
     dom = max(names, key=lambda n: stage_ms[n])
     achieved = kern_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    digest = source_digest(BWD_SOURCES[dom])
+    digest = source_digest("bwd_" + dom)
     gate_bytes = 4 if w.gate == "scalar" else 512
     compulsory = th * (4 * 256 + gate_bytes + 4 + 3 * 256 + gate_bytes + 4) + (n_s0 + 2) * STATE_BYTES * N * H
     path_gbs = compulsory / (ms_step * 1e-3) / 1e9
@@ -309,7 +317,7 @@ def backward_bench(args, w, x):
                      "frac": path_gbs / HBM_PEAK_GBS},
         "kernels_ms": stage_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for("bwd_" + dom, digest, w.name),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for("bwd_" + dom, w.name),
                      "algorithmic_bytes": kern_bytes[dom], "source_digest": digest},
     }
     if not args.no_cpu_baseline:
@@ -413,8 +421,8 @@ def train_bench(args, w, x):
     achieved = kern_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
     traffic, digest = None, None
     if dom != "forward":  # one kernel, with its own counter summary
-        digest = source_digest(BWD_SOURCES[dom])
-        traffic = traffic_for("bwd_" + dom, digest, w.name)
+        digest = source_digest("bwd_" + dom)
+        traffic = traffic_for("bwd_" + dom, w.name)
     gate_bytes = 4 if w.gate == "scalar" else 512
     forward_compulsory = th * (3 * 256 + gate_bytes + 4 + 256) + (2 * n_s0 + 1) * STATE_BYTES * N * H
     backward_compulsory = th * (4 * 256 + gate_bytes + 4 + 3 * 256 + gate_bytes + 4) + (n_s0 + 2) * STATE_BYTES * N * H
@@ -563,21 +571,26 @@ def main():
     tflops = counts["flops"] / (ms_step * 1e-3) / 1e12
     path_gbs = counts["bytes"] / (ms_step * 1e-3) / 1e9
 
+    # per kernel: mean launch time and its own algorithmic bytes (what it must read and
+    # write, including the intermediate records)
     kernels = {
-        "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th,
-                  ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_device.h", "kda_chunks.h"]),
-        "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * w.num_seqs * H * n_states,
-                  ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"]),
+        "intra": (intra_ms, INTRA_BYTES_PER_TH[w.gate] * th),
+        "inter": (inter_ms, INTER_BYTES_PER_TH * th + STATE_BYTES * w.num_seqs * H * n_states),
     }
     if args.fused:
         # one launch; its algorithmic bytes are the path's compulsory bytes
-        kernels = {"fused": (intra_ms, counts["bytes"], ["kda_inter_bf16.hip", "kda_ring.h", "kda_intra_wave.h",
-                                                         "kda_device.h", "kda_chunks.h"])}
+        kernels = {"fused": (intra_ms, counts["bytes"])}
     dom = max(kernels, key=lambda n: kernels[n][0])
-    dom_ms, dom_bytes, dom_src = kernels[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    digest = source_digest(dom_src)
-    traffic = traffic_for(dom, digest, w.name)
+    dom_ms, own_bytes = kernels[dom]
+    # The roofline's algorithmic bytes are the method's compulsory bytes per token and
+    # head (q, k, v, out bf16; g, beta fp32: 1540 at K = V = 128) times the token-heads
+    # one launch processes, plus the states it must read or write, over the dominant
+    # kernel's mean launch time; the kernel's own bytes (records included) are beside it.
+    achieved = counts["bytes"] / (dom_ms * 1e-3) / 1e9
+    own_achieved = own_bytes / (dom_ms * 1e-3) / 1e9
+    digest = source_digest(dom)
+    traffic = traffic_for(dom, w.name)
+    mfma_busy = mfma_busy_for(dom, w.name)
 
     rec = {
         "metric": (f"KDA prefill tokens/s + TFLOP/s (% roofline), H={H} T={T} K=V=128 bf16"
@@ -603,7 +616,9 @@ def main():
         "kernels_ms": {"fused": intra_ms} if args.fused else {"intra": intra_ms, "inter": inter_ms},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": dom_bytes, "source_digest": digest},
+                     "algorithmic_bytes": counts["bytes"], "ms": dom_ms,
+                     "kernel_own_bytes": own_bytes, "kernel_own_frac": own_achieved / HBM_PEAK_GBS,
+                     "mfma_busy": mfma_busy, "source_digest": digest},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w)
