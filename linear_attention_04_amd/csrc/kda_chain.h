@@ -333,6 +333,180 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
 }
 
 
+// ---------------------------------------------------------------------------
+// Whole-tile form: one compute wave per tile holds all 128 key rows of the tile's
+// 128 x 16 slice (the eight accumulator tiles M = 0 .. 7). There is no partner and
+// no exchange: the barrier a chunk step passes only hands ring slots over from the
+// producers, and nothing on the chain waits for another wave. A step does the two
+// halves' work of the split form in one wave with the same operations in the same
+// order (x0, x1 and y0, y1 below are the halves' partial products), so both forms
+// give bitwise equal outputs and states.
+struct TileOps {
+    bf16x8 w[4], qt[4];  // the four slabs of W and Q~
+    bf16x8 kd[8];        // K^d^T tiles 0 .. 7, each over both halves of the 32-long reduction
+    bf16x8 tb, mm;       // T' (hi | lo) and M (hi | lo)
+    float2 gam;
+    unsigned int vb[4];  // value tile column c, token rows 4 grp .. + 3 (as read; see tile_vv)
+};
+
+// [V; V] over the 32-long reduction from the four values read. Kept out of
+// read_tile_ops: formed there, right after the reads are issued, it makes the wave
+// wait for every read of the step in the middle of the state update.
+__device__ __forceinline__ bf16x8 tile_vv(const TileOps &o) {
+    const unsigned int v01 = o.vb[0] | (o.vb[1] << 16), v23 = o.vb[2] | (o.vb[3] << 16);
+    return __builtin_bit_cast(bf16x8, make_uint4(v01, v23, v01, v23));
+}
+
+template <int NW>
+__device__ __forceinline__ void read_tile_ops(TileOps &o, const char *slot, int vt, int lane) {
+    const int c = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + (s * 64 + lane) * 16);
+        o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + (s * 64 + lane) * 16);
+    }
+    typedef const volatile __attribute__((address_space(3))) unsigned long long lds_u64;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        lds_u64 *pk = (lds_u64 *)(slot + kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8);
+        const unsigned long long a = *pk;
+        const unsigned long long b = *pk;
+        o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b,
+                                                        (unsigned)(b >> 32)));
+    }
+    o.tb = *reinterpret_cast<const bf16x8 *>(slot + kRecTB + lane * 16);
+    o.mm = *reinterpret_cast<const bf16x8 *>(slot + kRecMM + lane * 16);
+    o.gam = *reinterpret_cast<const float2 *>(slot + kRecGAM + (grp * 32 + 2 * c) * 4);
+    const unsigned short *vt16 = reinterpret_cast<const unsigned short *>(slot + kVOff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.vb[i] = vt16[(4 * grp + i) * (NW * 16) + vt * 16 + c];
+}
+
+// Before the barrier: W S in two partial sums over key rows 0 .. 63 (x0) and
+// 64 .. 127 (x1, then minus T' V), the output's two partial sums (M V joins y0),
+// then the decay of all eight accumulator tiles.
+template <bool OUT>
+__device__ __forceinline__ void tile_part_a(const TileOps &o, f32x4 (&S)[8], f32x4 &x0, f32x4 &x1, f32x4 &y) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sb[s][i] = to_bf16(S[2 * s][i]);
+            sb[s][4 + i] = to_bf16(S[2 * s + 1][i]);
+        }
+    }
+    f32x4 y0, y1;
+    x0 = mfma_16x16x32(o.w[0], sb[0], zero);
+    x1 = mfma_16x16x32(o.w[2], sb[2], zero);
+    if (OUT) y0 = mfma_16x16x32(sb[0], o.qt[0], zero);
+    if (OUT) y1 = mfma_16x16x32(sb[2], o.qt[2], zero);
+    x0 = mfma_16x16x32(o.w[1], sb[1], x0);
+    x1 = mfma_16x16x32(o.w[3], sb[3], x1);
+    if (OUT) y0 = mfma_16x16x32(sb[1], o.qt[1], y0);
+    if (OUT) y1 = mfma_16x16x32(sb[3], o.qt[3], y1);
+    const bf16x8 vv = tile_vv(o);
+    x1 -= mfma_16x16x32(o.tb, vv, zero);  // - T' V
+    if (OUT) {
+        y0 = mfma_16x16x32(vv, o.mm, y0);  // + (M V)^T
+        y = y0 + y1;
+    }
+    decay_tile<0>(S[0], o.gam);
+    decay_tile<1>(S[1], o.gam);
+    decay_tile<2>(S[2], o.gam);
+    decay_tile<3>(S[3], o.gam);
+    decay_tile<4>(S[4], o.gam);
+    decay_tile<5>(S[5], o.gam);
+    decay_tile<6>(S[6], o.gam);
+    decay_tile<7>(S[7], o.gam);
+}
+
+// After the barrier: Delta = T' V - W S, the state update of all eight tiles and
+// the output store.
+template <bool OUT, int NW>
+__device__ __forceinline__ void tile_part_b(const TileOps &o, f32x4 (&S)[8], const f32x4 &x0, const f32x4 &x1,
+                                            const f32x4 &y, char *ochunk, int len, const LaneOffsets &lo) {
+    const f32x4 d = -(x0 + x1);
+    unsigned int h01, h23, l01, l23;
+    split_pair(d[0], d[1], h01, l01);
+    split_pair(d[2], d[3], h23, l23);
+    const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) S[m] = mfma_16x16x32(o.kd[m], db, S[m]);
+    if (OUT) {
+        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+    }
+}
+
+// The chunk loop of the whole-tile compute wave of tile vt; barriers as in
+// compute_wave (B_j publishes chunk j's ring slot).
+template <int DEPTH, bool OUT, int NW, class Sync>
+__device__ __forceinline__ void compute_wave_full(f32x4 (&S)[8], char *ring, int64_t nchunks, int64_t tok_rows,
+                                                  char *o0, size_t chunk_rows, int vt, int lane,
+                                                  const LaneOffsets &lo, Sync &sync) {
+    auto slot_of = [&](int64_t j) {
+        return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
+    };
+    auto len_of = [&](int64_t j) {
+        const int64_t rem = tok_rows - 16 * j;
+        return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
+    };
+    auto step = [&](int64_t j, const TileOps &cur, TileOps &next) {
+        f32x4 x0, x1, y;
+        tile_part_a<OUT>(cur, S, x0, x1, y);
+        sync.barrier(j + 1);  // B_{j+1}
+        read_tile_ops<NW>(next, slot_of(j + 1), vt, lane);
+        tile_part_b<OUT, NW>(cur, S, x0, x1, y, OUT ? o0 + (size_t)j * chunk_rows : nullptr, len_of(j), lo);
+    };
+    TileOps opa, opb;
+    sync.barrier(0);  // B_0
+    read_tile_ops<NW>(opa, slot_of(0), vt, lane);
+    int64_t j = 0;
+    for (; j + 2 <= nchunks; j += 2) {
+        step(j, opa, opb);
+        step(j + 1, opb, opa);
+    }
+    if (j < nchunks) step(j, opa, opb);
+}
+
+// compute_role for the whole-tile form: compute wave vt owns value columns
+// col0 + 16 vt .. + 15 and all 128 key rows.
+template <int DEPTH, bool OUT, int NW, class Sync>
+__device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, int pair, int col0,
+                                                  const SeqChunks &sc, size_t tok_bytes, size_t chunk_rows,
+                                                  LaneOffsets lo, const float *__restrict__ s0,
+                                                  unsigned short *__restrict__ out, float *__restrict__ sT,
+                                                  Sync &sync) {
+    const int c = lane & 15, grp = lane >> 4;
+    lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;
+    f32x4 S[8];
+    const size_t sbase = (size_t)pair * KD * VD + col0 + vt * 16 + c;
+    if (s0) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    wait_vmcnt<0>();  // as in compute_role: no state load left for the loop's counter waits
+    char *o0 = OUT ? reinterpret_cast<char *>(out) + tok_bytes : nullptr;
+    compute_wave_full<DEPTH, OUT, NW>(S, ring, sc.chunk_end - sc.chunk_begin, sc.tok_end - sc.tok_begin, o0,
+                                      chunk_rows, vt, lane, lo, sync);
+    if (sT) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
+    }
+}
+
+
 // The hardware workgroup barrier: every wave of the workgroup takes part.
 struct HwSync {
     __device__ __forceinline__ void barrier(int64_t) { kda::barrier(); }

@@ -38,14 +38,23 @@ namespace {
 
 // SAVE: every chunk's start state goes to `states` ([H][max_chunks] x 32 KiB
 // fragments), for a backward pass. OUT: the output is written (a recomputed forward
-// that only saves states writes neither output nor final state).
-template <int DEPTH, bool SAVE, bool OUT, int NW>
-__global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
+// that only saves states writes neither output nor final state). FULL: one compute
+// wave per tile (compute_role_full) instead of two (compute_role); the prefill's form.
+template <int NW, bool FULL>
+constexpr int inter_compute_waves() { return FULL ? NW : compute_waves<NW>(); }
+template <int NW, bool FULL>
+constexpr int inter_waves() { return inter_compute_waves<NW, FULL>() + kProducers; }
+template <int NW, bool FULL>
+constexpr int inter_xchg_bytes() { return FULL ? 0 : xchg_bytes<NW>(); }
+
+template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>
+__global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
     const char *__restrict__ records, char *__restrict__ states, int xccs) {
     static_assert(NW == 2 || NW == 4, "two or four value tiles per workgroup");
+    static_assert(!(FULL && SAVE), "the whole-tile form does not save chunk states");
     static_assert(DEPTH >= 3, "a slot is refilled two chunks after it was read");
     static_assert((DEPTH - 1) * per_wave1<NW>() < 64, "a producer's loads in flight must fit the 6-bit counter");
     extern __shared__ __attribute__((aligned(1024))) char ring[];
@@ -69,9 +78,9 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
 
-    if (wid >= compute_waves<NW>()) {
+    if (wid >= inter_compute_waves<NW, FULL>()) {
         // ---- producer ----
-        const int p = wid - compute_waves<NW>();
+        const int p = wid - inter_compute_waves<NW, FULL>();
         const char *rec0 = records + ((size_t)h * max_chunks + sc.chunk_begin) * kRecBytesBf16;  // head-major
         const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
         auto len_of = [&](int64_t j) {
@@ -103,25 +112,30 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_inter_bf16_kernel(
         return;
     }
 
-    char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
     HwSync sync;
+    if (FULL) {
+        compute_role_full<DEPTH, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
+                                          OUT ? sT : nullptr, sync);
+        return;
+    }
+    char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
     compute_role<DEPTH, SAVE, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
                                        OUT ? sT : nullptr, sync, st);
 }
 
-template <int DEPTH, bool SAVE, bool OUT, int NW>
+template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>
 hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                   const Geometry &geo, const void *ws, const DeviceShape &dev, hipStream_t stream) {
     const int64_t blocks = (int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / NW);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
-    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW>;
+    auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW, FULL>;
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * waves<NW>()), lds, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * inter_waves<NW, FULL>()), lds, stream,
                        static_cast<const unsigned short *>(v), cu_seqlens, chunk_off, s0,
                        static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks,
                        base + geo.off_records, SAVE ? const_cast<char *>(base) + geo.off_states : nullptr,
@@ -224,9 +238,10 @@ hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float 
     DeviceShape dev;
     const hipError_t e = device_shape(&dev);
     if (e != hipSuccess) return e;
+    constexpr bool FULL = OUT && !SAVE;
     if ((int64_t)round_to_xccs(geo.N * geo.H, dev.xccs) * (kTiles / 2) <= dev.cus)
-        return launch<8, SAVE, OUT, 2>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
-    return launch<7, SAVE, OUT, 4>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
+        return launch<8, SAVE, OUT, 2, FULL>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
+    return launch<FULL ? 8 : 7, SAVE, OUT, 4, FULL>(v, cu_seqlens, s0, out, sT, geo, ws, dev, stream);
 }
 
 }  // namespace
