@@ -145,14 +145,16 @@ def generate_on_device(w, keep_heads, threads: int = 16):
 # ---------------------------------------------------------------------------
 # backward pass
 
-# Tolerances per gradient tensor (bf16 io). Relative to the tensor: rel-L2 over the
-# whole tensor, and max|err| against the tensor's largest magnitude. The forward's
-# rel-L2 bar (5e-3, one bf16-operand state product before the output) doubled, since
-# every gradient passes two bf16-operand state products in sequence (the state gradient
-# stored in bf16, then a product with the bf16 states); the absolute bar becomes
-# relative because the gradients span about three decades of magnitude.
-BWD_REL_L2 = 1e-2
-BWD_MAX_REL = 2e-2
+# Tolerances per gradient tensor (bf16 io), relative to the tensor because the gradients
+# span about three decades of magnitude: rel-L2 over the whole tensor, and max|err|
+# against the tensor's largest magnitude. Derived from the bf16 rounding model
+# (tests/rounding_model.py), which the GPU matches to a few per cent: on the workloads'
+# value recipes it predicts rel-L2 1.7e-3 .. 3.6e-3 and max|err| up to 3.8e-3 of the
+# largest magnitude for every gradient (pinned in test_rounding_model.py). The bars keep
+# 30% over the largest rel-L2 and 2.5x over the largest max|err| (extremes grow with the
+# number of elements; the full-size tests see 10^7 of them).
+BWD_REL_L2 = 5e-3
+BWD_MAX_REL = 1e-2
 
 _ALIGN = 256
 _REC_BYTES = 14848
@@ -233,6 +235,25 @@ def assert_close_rel(name, got, ref, rel_l2=None, max_rel=None):
     assert rel <= rel_l2, f"{name}: rel-L2 {rel:.3e} > {rel_l2}"
     assert max_abs <= max_rel * max(scale, 1e-30), f"{name}: max|err| {max_abs:.3e} > {max_rel} * {scale:.3e}"
     return max_abs, rel
+
+
+# The GPU's distance to the oracle against the rounding model's, on the same inputs:
+# the model rounds where the kernels round, so the two agree closely (measured: within
+# 0.9% over every tensor of the parity tests); the band allows for the fp32 summation
+# order and, in small tensors, the few bf16 results that round the other way.
+MODEL_BAND = 0.1
+MODEL_FLOOR = 2e-4
+
+
+def assert_model_band(name, got, ref, model):
+    """rel-L2 of `got` (GPU) against `ref` (oracle) within MODEL_BAND of the rounding
+    model's rel-L2 against the same reference (plus MODEL_FLOOR)."""
+    from tests import rounding_model as rm
+
+    e_gpu, e_model = rm.rel_l2(got, ref), rm.rel_l2(model, ref)
+    print(f"  {name}: GPU rel-L2 {e_gpu:.3e}, rounding model {e_model:.3e}", flush=True)
+    assert abs(e_gpu - e_model) <= MODEL_BAND * e_model + MODEL_FLOOR, \
+        f"{name}: GPU rel-L2 {e_gpu:.3e} outside the rounding model's {e_model:.3e} +- {MODEL_BAND:.0%}"
 
 
 def first_heads(x: dict, n: int) -> dict:

@@ -9,6 +9,7 @@ import oracle
 from linear_attention_04_amd import inputs
 from oracle import reference
 from tests import gpu_util as gu
+from tests import rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -40,9 +41,10 @@ def _check(w, x, d_out, d_fs, packed, use_dfs=True):
     d = gu.upload_backward(x, d_out, d_fs, packed)
     got = gu.run_gpu_backward(d)
     ref = gu.run_oracle_backward(x, d_out, d_fs, packed)
-    for name in GRADS:
+    model = rounding_model.backward(x if packed else dict(x, cu_seqlens=None), d_out, d_fs)
+    for name in GRADS + ("d_initial_state",):
         gu.assert_close_rel(name, gu.to_host(got[name]), ref[name])
-    gu.assert_close_rel("d_initial_state", gu.to_host(got["d_initial_state"]), ref["d_initial_state"])
+        gu.assert_model_band(name, gu.to_host(got[name]), ref[name], model[name])
     return d, got, ref
 
 

@@ -7,6 +7,7 @@ import pytest
 
 from linear_attention_04_amd import inputs
 from tests import gpu_util as gu
+from tests import rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,10 @@ def _check(w, x, packed):
     ro, rs = gu.run_oracle(x, packed)
     gu.assert_close("out", gu.to_host(out), ro, w.bf16)
     gu.assert_close("final_state", gu.to_host(fs), rs, w.bf16)
+    if w.bf16 and w.total_tokens > 0:
+        mo, mfs = rounding_model.forward(x if packed else dict(x, cu_seqlens=None))
+        gu.assert_model_band("out", gu.to_host(out), ro, mo)
+        gu.assert_model_band("final_state", gu.to_host(fs), rs, mfs)
     return d, out, fs
 
 
