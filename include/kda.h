@@ -55,7 +55,9 @@
  * and outputs stay inside fp32's range. NaN or infinite g are not supported.
  *
  * Size limits (KDA_ERR_ARG beyond them, and kda_workspace_bytes returns 0):
- * 0 <= T <= 2^31 - 1, 1 <= H <= 2^16, 1 <= N <= 2^24 and N * H < 2^25.
+ * 0 <= T <= 2^31 - 1, 1 <= H <= 2^16, 1 <= N <= 2^20 and N * H < 2^25. (The
+ * workspace holds a record for every chunk slot a batch may need, (T + 15 N) / 16
+ * per head: at N = 2^20 that is already ~15 GB per head.)
  */
 #ifndef KDA_H
 #define KDA_H
@@ -258,7 +260,7 @@ int kda_chunk_prefill_for_backward(const void *q, const void *k, const void *v, 
  *              [0, num_seqs] at which cu_seqlens[0] = 0, cu_seqlens[n - 1] <=
  *              cu_seqlens[n] or cu_seqlens[num_seqs] = total_tokens fails, else -1.
  * Asynchronous on `stream` like every entry point: read *result after the stream has
- * passed the call. KDA_ERR_ARG for NULL pointers, num_seqs outside [1, 2^24] or
+ * passed the call. KDA_ERR_ARG for NULL pointers, num_seqs outside [1, 2^20] or
  * total_tokens outside [0, 2^31 - 1]; KDA_ERR_ALIGN for misaligned pointers. */
 int kda_check_seqlens(const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t *result,
                       void *stream);

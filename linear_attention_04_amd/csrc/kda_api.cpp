@@ -103,7 +103,7 @@ int make_geometry(const kda_dims_t *d, Geometry *g) {
     if (d->total_tokens < 0 || d->num_heads < 1 || d->head_k < 1 || d->head_v < 1 || d->num_seqs < 1 ||
         (d->gate_kind != KDA_GATE_CHANNEL && d->gate_kind != KDA_GATE_SCALAR))
         return KDA_ERR_ARG;
-    if (d->total_tokens > (int64_t)INT32_MAX || d->num_seqs > (1 << 24) || d->num_heads > (1 << 16))
+    if (d->total_tokens > (int64_t)INT32_MAX || d->num_seqs > kMaxSeqs || d->num_heads > (1 << 16))
         return KDA_ERR_ARG;
     if (!supported(d)) return KDA_ERR_UNSUPPORTED;
     g->T = d->total_tokens;
@@ -375,7 +375,7 @@ int kda_chunk_prefill_backward(const void *q, const void *k, const void *v, cons
 int kda_check_seqlens(const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t *result,
                       void *stream) {
     if (cu_seqlens == nullptr || result == nullptr) return KDA_ERR_ARG;
-    if (num_seqs < 1 || num_seqs > (1 << 24) || total_tokens < 0 || total_tokens > (int64_t)INT32_MAX)
+    if (num_seqs < 1 || num_seqs > kda::kMaxSeqs || total_tokens < 0 || total_tokens > (int64_t)INT32_MAX)
         return KDA_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(result) & 3u) != 0)
         return KDA_ERR_ALIGN;

@@ -10,6 +10,7 @@
 namespace kda {
 
 constexpr int kChunk = 16;
+constexpr int kMaxSeqs = 1 << 20;  // packed sequences per call
 
 // bf16 K = V = 128 record of one (chunk, head), written by the intra-chunk kernel and
 // read by the inter-chunk kernel. Byte offsets:

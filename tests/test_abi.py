@@ -68,17 +68,18 @@ def test_workspace_bytes(lib):
 
 
 def test_size_limits(lib):
-    # the largest accepted sizes (include/kda.h): 2^31 - 1 tokens, 2^16 heads, 2^24
+    # the largest accepted sizes (include/kda.h): 2^31 - 1 tokens, 2^16 heads, 2^20
     # packed sequences, N * H < 2^25
     assert kda.kda_workspace_bytes(dims(T=(1 << 31) - 1)) > 0
     assert kda.kda_workspace_bytes(dims(H=1 << 16)) > 0
-    assert kda.kda_workspace_bytes(dims(N=1 << 24, T=1 << 24, H=1)) > 0
-    assert kda.kda_workspace_bytes(dims(N=(1 << 24) - 1, T=1 << 24, H=2)) > 0
+    assert kda.kda_workspace_bytes(dims(N=1 << 20, T=1 << 24, H=1)) > 0
+    assert kda.kda_workspace_bytes(dims(N=1 << 20, T=1 << 24, H=31)) > 0
+    assert kda.kda_workspace_bytes(dims(N=(1 << 20) - 1, T=1 << 24, H=32)) > 0
     # one past each limit is rejected (no size computation overflows into a small workspace)
     assert kda.kda_workspace_bytes(dims(T=1 << 31)) == 0
     assert kda.kda_workspace_bytes(dims(H=(1 << 16) + 1)) == 0
-    assert kda.kda_workspace_bytes(dims(N=(1 << 24) + 1, T=1 << 25, H=1)) == 0
-    assert kda.kda_workspace_bytes(dims(N=1 << 24, T=1 << 24, H=2)) == 0       # N * H = 2^25
+    assert kda.kda_workspace_bytes(dims(N=(1 << 20) + 1, T=1 << 25, H=1)) == 0
+    assert kda.kda_workspace_bytes(dims(N=1 << 20, T=1 << 24, H=32)) == 0       # N * H = 2^25
     assert kda.kda_workspace_bytes(dims(N=0)) == 0
     b = Buf()
     p = b.at()
@@ -221,7 +222,7 @@ def test_check_seqlens_argument_checks(lib):
     assert kda.kda_check_seqlens(None, 1, 16, p, None) == kda.KDA_ERR_ARG
     assert kda.kda_check_seqlens(p, 1, 16, None, None) == kda.KDA_ERR_ARG
     assert kda.kda_check_seqlens(p, 0, 16, p, None) == kda.KDA_ERR_ARG
-    assert kda.kda_check_seqlens(p, (1 << 24) + 1, 16, p, None) == kda.KDA_ERR_ARG
+    assert kda.kda_check_seqlens(p, (1 << 20) + 1, 16, p, None) == kda.KDA_ERR_ARG
     assert kda.kda_check_seqlens(p, 1, -1, p, None) == kda.KDA_ERR_ARG
     assert kda.kda_check_seqlens(p, 1, 1 << 31, p, None) == kda.KDA_ERR_ARG
     # int32 arrays need 4-byte alignment only
