@@ -55,6 +55,26 @@ BWD_BYTES_PER_TH = {
 }
 
 
+# Untimed steps before the warm-up: from idle the clocks take ~40 back-to-back steps
+# (~20 ms) to settle, so a short warm-up alone would time the ramp. The timed region is
+# still exactly the K steps after the W warm-up steps.
+SETTLE_MS = 100.0
+
+
+def settle(step) -> int:
+    """Run untimed steps until SETTLE_MS of wall time has passed; returns how many."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +202,7 @@ def decode_bench(args):
         if st:
             raise kda.KdaError(st, "decode")
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -203,7 +224,7 @@ def decode_bench(args):
         "metric": "KDA decode step tokens/s (one token per sequence, state update in place)",
         "value": B / (ms_step * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_k": 128, "head_v": 128, "gate": args.gate},
         "kernels_ms": {"decode": kern_ms},
@@ -275,6 +296,7 @@ def backward_bench(args, w, x):
         if bad:
             raise kda.KdaError(bad[0], "backward")
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -309,7 +331,7 @@ def backward_bench(args, w, x):
                    f"H={H} T={T} K=V=128 bf16" + (" (scalar gate)" if w.gate == "scalar" else "")),
         "value": T / (ms_step * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128, "num_seqs": N,
                    "initial_state": s0 is not None, "chunk": 16, "gate": w.gate, "pass": "backward"},
@@ -389,6 +411,7 @@ def train_bench(args, w, x):
         if bad:
             raise kda.KdaError(bad[0], "training step")
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -433,7 +456,7 @@ def train_bench(args, w, x):
                    + (" (scalar gate)" if w.gate == "scalar" else "")),
         "value": T / (ms_step * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "heads": H, "tokens": T, "head_k": 128, "head_v": 128, "num_seqs": N,
                    "initial_state": s0 is not None, "chunk": 16, "gate": w.gate, "pass": "train"},
@@ -541,6 +564,7 @@ def main():
         if st or st2:
             raise kda.KdaError(st or st2, "prefill")
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -600,6 +624,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
