@@ -43,7 +43,10 @@ def test_fullsize_all_heads(name):
 
 
 def test_fullsize_long_context_sampled_heads():
-    _run("long_h64_t131072_s0", [0, 21, 42, 63])
+    """Eight of the 64 heads, one on each XCD (the recurrent kernel places (sequence,
+    head) pair p on XCD p mod 8) and spread over the head range; every head runs the
+    same 2-tile workgroup form, so the sample covers each distinct launch position."""
+    _run("long_h64_t131072_s0", [0, 9, 18, 27, 36, 45, 54, 63])
 
 
 def test_fullsize_scalar_gate_all_heads():
