@@ -48,12 +48,12 @@ HBM_PEAK_GBS = 8000.0
 # matches.
 KERNEL_SOURCES = {
     "intra": ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_gate_exact.h", "kda_device.h", "kda_chunks.h"],
-    "inter": ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
-    "fused": ["kda_inter_bf16.hip", "kda_ring.h", "kda_intra_wave.h", "kda_gate_exact.h", "kda_device.h",
-              "kda_chunks.h"],
+    "inter": ["kda_inter_bf16.hip", "kda_chain.h", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
+    "fused": ["kda_inter_bf16.hip", "kda_chain.h", "kda_ring.h", "kda_intra_wave.h", "kda_gate_exact.h",
+              "kda_device.h", "kda_chunks.h"],
     "decode": ["kda_decode.hip", "kda_device.h"],
     "bwd_records": ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_gate_exact.h", "kda_device.h", "kda_chunks.h"],
-    "bwd_states": ["kda_inter_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
+    "bwd_states": ["kda_inter_bf16.hip", "kda_chain.h", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
     "bwd_state_grad": ["kda_state_grad_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
     "bwd_token_grad": ["kda_grad_bf16.hip", "kda_gate_exact.h", "kda_device.h", "kda_chunks.h"],
 }
