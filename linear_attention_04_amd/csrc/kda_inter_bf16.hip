@@ -8,8 +8,10 @@
 // of one head as NW 16-column tiles, and shares one copy of each chunk's operands
 // between them. NW = 2 while each 2-tile workgroup can have a CU of its own, else 4.
 // Each tile's 128 x 16 slice of S lives in MFMA accumulator registers for the whole
-// sequence, split by rows over two waves (see the compute waves below), so that every
-// SIMD of the CU runs NW / 2 links of recurrence chains.
+// sequence: in the prefill, in one compute wave per tile (compute_role_full); in the
+// training forward, which also saves every chunk's start state, split by rows over two
+// waves that swap partial products through LDS (compute_role). Both forms give bitwise
+// equal results (kda_chain.h).
 //
 // Per chunk, with S the state at the chunk start and V the chunk's value tile
 // (T', M, W, Q~, K^d and gamma from the intra-chunk kernel):
@@ -21,15 +23,16 @@
 // to bf16, directly the B operand of W S and Q~ S, because the intra-chunk kernel
 // stores W and Q~ with matching channel order; Delta's accumulator layout is the B
 // operand of K^d^T Delta. Across lanes, only gamma moves (DPP broadcasts inside
-// 16-lane rows); across waves, only the partial W S and Q~ S (through LDS).
+// 16-lane rows); across waves, nothing in the one-wave form, and the partial W S and
+// Q~ S (through LDS) in the two-wave form.
 //
 // Memory pipeline: a chunk step takes a few hundred cycles while an HBM load takes
 // on the order of a microsecond, so each workgroup keeps a ring of DEPTH chunk
 // slots in LDS that two producer waves fill with direct buffer->LDS loads
 // (buffer_load_dwordx4 ... lds) several chunks ahead; the loads hold no registers.
 // A producer waits (s_waitcnt vmcnt) for its own part of a chunk, then one
-// s_barrier per chunk publishes the slot to the compute waves (and, at the same
-// time, the previous chunk's partial products between the two halves of a tile).
+// s_barrier per chunk publishes the slot to the compute waves (and, in the two-wave
+// form, the previous chunk's partial products between the two halves of a tile).
 #include "kda_chain.h"
 #include "kda_intra_wave.h"
 

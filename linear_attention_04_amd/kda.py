@@ -331,8 +331,10 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=Non
     _check_outputs(v, dims, out, final_state)
     if workspace is None:
         workspace = workspace_for(dims, q.device)
-    elif _nbytes(workspace) < kda_workspace_bytes(dims) or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a device buffer of at least {kda_workspace_bytes(dims)} bytes")
+    elif _nbytes(workspace) < kda_workspace_bytes(dims) or not workspace.is_cuda or not workspace.is_contiguous() \
+            or workspace.device != q.device:
+        raise ValueError(f"workspace must be a contiguous buffer of at least {kda_workspace_bytes(dims)} bytes "
+                         f"on {q.device}")
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if final_state is True:
@@ -418,9 +420,9 @@ def _backward_workspace(dims, device, workspace, allocate=True):
         if not allocate:
             raise ValueError("workspace is required: pass the one chunk_prefill_for_backward filled")
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if _nbytes(workspace) < nbytes or not workspace.is_cuda \
-            or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous device buffer of at least {nbytes} bytes")
+    if _nbytes(workspace) < nbytes or not workspace.is_cuda or not workspace.is_contiguous() \
+            or workspace.device != torch.device(device):
+        raise ValueError(f"workspace must be a contiguous buffer of at least {nbytes} bytes on {device}")
     return workspace
 
 
