@@ -202,11 +202,14 @@ def decode_bench(args):
         if st:
             raise kda.KdaError(st, "decode")
 
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Nothing runs between the warm-up and the timed steps but the synchronisation (the
+    # checks and event allocations come first): an idle GPU lowers its clocks within
+    # milliseconds, and the first timed steps would pay for it.
     settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     bounds[0].record(stream)
     for i in range(args.steps):
@@ -296,15 +299,19 @@ def backward_bench(args, w, x):
         if bad:
             raise kda.KdaError(bad[0], "backward")
 
-    settle_steps = settle(step)
-    for _ in range(args.warmup):
-        step()
+    step()
     torch.cuda.synchronize()
     if not all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv, dg, dbeta)):
         print("non-finite gradient", file=sys.stderr)
         return 1
     start = torch.cuda.Event(enable_timing=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Nothing runs between the warm-up and the timed steps but the synchronisation (the
+    # checks and event allocations come first): an idle GPU lowers its clocks within
+    # milliseconds, and the first timed steps would pay for it.
+    settle_steps = settle(step)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -411,15 +418,19 @@ def train_bench(args, w, x):
         if bad:
             raise kda.KdaError(bad[0], "training step")
 
-    settle_steps = settle(step)
-    for _ in range(args.warmup):
-        step()
+    step()
     torch.cuda.synchronize()
     if not all(bool(torch.isfinite(t.float()).all()) for t in (out, dq, dk, dv, dg, dbeta)):
         print("non-finite output or gradient", file=sys.stderr)
         return 1
     start = torch.cuda.Event(enable_timing=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Nothing runs between the warm-up and the timed steps but the synchronisation (the
+    # checks and event allocations come first): an idle GPU lowers its clocks within
+    # milliseconds, and the first timed steps would pay for it.
+    settle_steps = settle(step)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -564,9 +575,7 @@ def main():
         if st or st2:
             raise kda.KdaError(st or st2, "prefill")
 
-    settle_steps = settle(step)
-    for _ in range(args.warmup):
-        step()
+    step()
     torch.cuda.synchronize()
     if not bool(torch.isfinite(out.float()).all()):
         print("non-finite output", file=sys.stderr)
@@ -574,6 +583,12 @@ def main():
 
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Nothing runs between the warm-up and the timed steps but the synchronisation (the
+    # checks and event allocations come first): an idle GPU lowers its clocks within
+    # milliseconds, and the first timed steps would pay for it.
+    settle_steps = settle(step)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     bounds[0].record(stream)
