@@ -3,8 +3,8 @@ library's kernels under bench.py, against the MI355X peaks.
 
 Two steps, both from the repository root:
 
-    python -m linear_attention_04_amd.rocprof_report run [--only h64 ...] [--dir gpurun_out/prof]
-    python -m linear_attention_04_amd.rocprof_report summarize [--only h64 ...] [--dir gpurun_out/prof]
+    python -m linear_attention_04_amd.rocprof_report run [--only h64 ...] [--dir rocprof_out]
+    python -m linear_attention_04_amd.rocprof_report summarize [--only h64 ...] [--dir rocprof_out]
 
 ``run`` (on the GPU machine) starts, for every profiled bench mode, four rocprofv3
 passes over ``python3 bench.py`` as child processes: a kernel trace with statistics,
@@ -276,10 +276,10 @@ def summarize(names, in_dir: str, read_scale: float, write_scale: float, scale_s
         except FileNotFoundError:
             sq = {}
         b = bench_line(os.path.join(in_dir, f"{name}_trace.log")) or {}
-        cmds = commands(mode, "gpurun_out/prof")
+        cmds = commands(mode, in_dir)
         lines = [f"# {mode.title}", "", f"Workload `{mode.workload}`. Made by "
-                 "`python -m linear_attention_04_amd.rocprof_report run --only " + name + "` (then `summarize`), "
-                 "which runs:", "", "```"]
+                 "`python -m linear_attention_04_amd.rocprof_report run --only " + name + f" --dir {in_dir}` "
+                 "(then `summarize`), which runs:", "", "```"]
         lines += [" ".join(argv) for _, argv in cmds]
         lines += ["```", "",
                   "| kernel | calls | avg us | min us | max us | HBM read MB | HBM write MB | MFMA busy | "
@@ -333,7 +333,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("step", choices=("run", "summarize"))
     ap.add_argument("--only", nargs="*", default=None, help=f"modes (default: all): {' '.join(MODES)} copy")
-    ap.add_argument("--dir", default=os.path.join("gpurun_out", "prof"))
+    ap.add_argument("--dir", default="rocprof_out", help="where the passes write (run) and are read from")
     a = ap.parse_args(argv)
     names = a.only or list(MODES)
     if a.step == "run":
