@@ -21,6 +21,7 @@ import pytest
 
 from linear_attention_04_amd import inputs
 from tests import gpu_util as gu
+from tests import rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +113,10 @@ def _forward(w, x, packed=False, fused=True):
     ro, rs = gu.run_oracle(x, packed)
     gu.assert_close("out", gu.to_host(out), ro, w.bf16)
     gu.assert_close("final_state", gu.to_host(fs), rs, w.bf16)
+    if w.bf16:  # the rounding model takes the per-pair path where the kernels do
+        mo, mfs = rounding_model.forward(x if packed else dict(x, cu_seqlens=None))
+        gu.assert_model_band("out", gu.to_host(out), ro, mo)
+        gu.assert_model_band("final_state", gu.to_host(fs), rs, mfs)
     if fused and w.bf16:
         from linear_attention_04_amd import kda
 

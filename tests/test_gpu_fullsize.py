@@ -8,6 +8,7 @@ import pytest
 import oracle
 from linear_attention_04_amd import inputs
 from tests import gpu_util as gu
+from tests import rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +23,8 @@ def _need_gpu():
     kda.load_library()
 
 
-def _run(name, keep, w=None):
+def _run(name, keep, w=None, model=False):
+    """model: also hold the GPU's error to the bf16 rounding model's on the same heads."""
     w = w or inputs.WORKLOADS[name]
     print(f"workload {name}: heads kept for the oracle {keep}", flush=True)
     dev, host = gu.generate_on_device(w, keep)
@@ -35,11 +37,16 @@ def _run(name, keep, w=None):
     got_s = gu.to_host(fs[:, keep])
     gu.assert_close("out", got_o, ro, True)
     gu.assert_close("final_state", got_s, rs, True)
+    if model:
+        mo, mfs = rounding_model.forward(host if packed else dict(host, cu_seqlens=None))
+        gu.assert_model_band("out", got_o, ro, mo)
+        gu.assert_model_band("final_state", got_s, rs, mfs)
 
 
 @pytest.mark.parametrize("name", ["fixed_h64_t8192", "fixed_h96_t8192_s0", "varlen_h96_t8192_n8"])
 def test_fullsize_all_heads(name):
-    _run(name, list(range(inputs.WORKLOADS[name].heads)))
+    # the headline workload is also held to the rounding model (~30 s of CPU)
+    _run(name, list(range(inputs.WORKLOADS[name].heads)), model=name == "fixed_h64_t8192")
 
 
 def test_fullsize_long_context_sampled_heads():
