@@ -109,6 +109,51 @@ def test_fp32_small(lib):
     _check(lib, w, inputs.generate(w), False)
 
 
+@pytest.mark.parametrize("case", ["fits", "segments"])
+def test_graph_capture_and_replay(lib, case):
+    """The use the entry point exists for: captured once in a HIP graph (it allocates
+    nothing, so the capture holds only its kernels) and replayed on new inputs, with
+    eager work and synchronisation between replays; every replay equals an eager
+    kda_chunk_prefill on the same inputs, bit for bit."""
+    torch = gu.torch_mod()
+    kda = lib
+    H, T = (4, 300) if case == "fits" else (48, 2000)
+    mk = lambda seed: inputs.custom_workload(f"na_graph_{case}_{seed}", seed, heads=H, total_tokens=T,  # noqa: E731
+                                             has_initial_state=True)
+    w = mk(720)
+    d = gu.upload(inputs.generate(w), True, False)
+    dims = kda.make_dims(d["q"], d["v"], None, g=d["g"])
+    assert (kda.kda_workspace_bytes(dims) > kda.KDA_NOALLOC_SCRATCH_BYTES) == (case == "segments")
+    out = torch.empty_like(d["v"])
+    fs = torch.empty_like(d["initial_state"])
+    p = lambda t: t.data_ptr()  # noqa: E731
+
+    def call():
+        st = kda.kda_chunk_prefill_noalloc(p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]), None,
+                                           p(d["initial_state"]), p(out), p(fs), dims,
+                                           torch.cuda.current_stream().cuda_stream)
+        assert st == kda.KDA_OK, kda.kda_status_string(st)
+
+    call()  # eager first: the device's buffer address is looked up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xr = inputs.generate(mk(721 + rep))
+        dr = gu.upload(xr, True, False)
+        for name in ("q", "k", "v", "g", "beta", "initial_state"):
+            d[name].copy_(dr[name])
+        ref_out, ref_fs = gu.run_gpu(dr)  # eager kda_chunk_prefill on its own workspace
+        out.zero_()
+        fs.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"case {case}: replay {rep}", flush=True)
+        assert torch.equal(out, ref_out) and torch.equal(fs, ref_fs), f"replay {rep} differs from the eager call"
+
+
 def test_packed_batch_too_large_is_rejected(lib):
     torch = gu.torch_mod()
     kda = lib
