@@ -26,13 +26,17 @@
 // the keys across lanes, exactly (the values are bf16 and the accumulator fp32), and the
 // same identity product turns a token-per-lane tile into a column-per-lane tile. Every
 // layout change in this kernel is such an exact MFMA. Each state fragment is loaded
-// once; LDS holds the 16 x 16 matrices and the K+ and K^d operands.
+// once; LDS holds the 16 x 16 matrices and the K+ and K^d operands. q, k and g are
+// read twice, for the chunk factors and again for the per-channel gradients: at two
+// waves per SIMD neither the registers nor LDS can keep them in between. The second
+// read is issued before the 16 x 16 backward, so that its latency is hidden.
 #include <type_traits>
 
 #include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_gate_exact.h"
 #include "kda_internal.h"
+#include "kda_ring.h"  // buffer descriptors and counter waits for the loads into LDS
 
 namespace kda {
 namespace {
@@ -370,6 +374,32 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     store_tile<256>(reinterpret_cast<const char *>(L.dt), reinterpret_cast<char *>(dv + ((size_t)start * H + h) * VD),
                     (size_t)H * VD * 2, len, lane);
     wave_sync();
+    // The key tiles need q, k and g again. q and k go straight to the K+ / K^d area,
+    // free from here on, in the swizzled tile layout that later gathers dq and dk (each
+    // lane reads its inputs there before writing its outputs in the same place); rows
+    // past the chunk read as zero. g goes to registers, which the 16 x 16 backward
+    // leaves free. Both are in flight during that backward.
+    {
+        const unsigned int rowb = (unsigned int)H * KD * 2;  // one token row of q or k, bytes
+        const size_t row0 = ((size_t)start * H + h) * KD;
+        const int bytes = (int)((len - 1) * rowb + KD * 2);  // H <= 2^16: below 2^28
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q + row0, bytes), rk = rsrc(k + row0, bytes);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // rows 4s .. 4s + 3, 1 KiB per wave-wide load
+            const int r = 4 * s + (lane >> 4), j = (lane & 15) ^ r;  // LDS chunk lane & 15 holds chunk j
+            const unsigned int off = (unsigned int)r * rowb + 16u * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(reinterpret_cast<char *>(L.kps) + 1024 * s),
+                                                     16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(reinterpret_cast<char *>(L.kds) + 1024 * s),
+                                                     16, off, 0, 0, 0);
+        }
+    }
+    float4 gk[8];  // g of token c, channels 16kt + 4grp .. + 3
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+        gk[kt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!SCALAR_GATE && row_ok) gk[kt] = *reinterpret_cast<const float4 *>(g + krow + 16 * kt + 4 * grp);
+    }
 
     // ================= 3. the 16 x 16 backward =================
     float dbeta_c;
@@ -439,6 +469,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     const SplitDup m_dacol = split_dup(dacol);
     const SplitDup m_dprow = split_dup(*reinterpret_cast<const f32x4 *>(&L.dp[c * 16 + 4 * grp]));
     const SplitDup m_dpcol = split_dup(dpcol);
+    wait_vmcnt<0>();  // q and k have landed in LDS
     wave_sync();  // the matrices' area now gathers dg, the K+/K^d area dq and dk
     char *tg = reinterpret_cast<char *>(L.a);
     char *tq = reinterpret_cast<char *>(L.kps);
@@ -447,18 +478,16 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     // so the products of A~ and P with the gates are differentiated pair by pair.
     auto key_tile = [&](int kt, auto exact_tag) {
         constexpr bool EXACT = decltype(exact_tag)::value;
-        const size_t kc = krow + 16 * kt + 4 * grp;  // channels 16kt + 4grp + i of token c
-        f32x4 kk = zero4(), qq = zero4(), G = zero4();
-        if (row_ok) {
-            kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(k + kc));
-            qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(q + kc));
-            if (SCALAR_GATE) {
-                const float gs = g[(size_t)tok * H + h];
-                G = f32x4{gs, gs, gs, gs};
-            } else {
-                const float4 gv = *reinterpret_cast<const float4 *>(g + kc);
-                G = f32x4{gv.x, gv.y, gv.z, gv.w};
-            }
+        const int cb = 2 * (16 * kt + 4 * grp);  // byte of channel 16kt + 4grp in a bf16 row
+        // channels 16kt + 4grp + i of token c
+        const f32x4 kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(tk + tile_off<256>(c, cb)));
+        const f32x4 qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(tq + tile_off<256>(c, cb)));
+        f32x4 G;
+        if (SCALAR_GATE) {
+            const float gs = row_ok ? g[(size_t)tok * H + h] : 0.f;
+            G = f32x4{gs, gs, gs, gs};
+        } else {
+            G = f32x4{gk[kt].x, gk[kt].y, gk[kt].z, gk[kt].w};
         }
         // ga: the gradient reaching k through A~ and P (dK^ exp(G - G_ref) + dK~ exp(G_ref - G)),
         // gq: reaching q through P (dQ^ exp(G - G_ref)), gg: reaching G through them
@@ -550,7 +579,6 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             if (c == len - 1) dG += dgc;
             dgv[i] = row_suffix_sum(dG);
         }
-        const int cb = 2 * (16 * kt + 4 * grp);  // byte of channel 16kt + 4grp in a bf16 row
         *reinterpret_cast<bf16x4 *>(tk + tile_off<256>(c, cb)) = to_bf16x4(dkq);
         *reinterpret_cast<bf16x4 *>(tq + tile_off<256>(c, cb)) = to_bf16x4(dqq);
         if (SCALAR_GATE) {

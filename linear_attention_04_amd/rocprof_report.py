@@ -55,7 +55,7 @@ KERNEL_SOURCES = {
     "bwd_records": ["kda_intra_bf16.hip", "kda_intra_wave.h", "kda_gate_exact.h", "kda_device.h", "kda_chunks.h"],
     "bwd_states": ["kda_inter_bf16.hip", "kda_chain.h", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
     "bwd_state_grad": ["kda_state_grad_bf16.hip", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
-    "bwd_token_grad": ["kda_grad_bf16.hip", "kda_gate_exact.h", "kda_device.h", "kda_chunks.h"],
+    "bwd_token_grad": ["kda_grad_bf16.hip", "kda_gate_exact.h", "kda_ring.h", "kda_device.h", "kda_chunks.h"],
 }
 
 SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU",
