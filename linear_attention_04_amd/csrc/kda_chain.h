@@ -28,10 +28,11 @@ constexpr int VD = 128;
 constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 
 
-// A workgroup covers NW tiles of 16 value columns with 2 NW compute waves (two per
-// tile) and two producer waves (NW = 2, or 4 when 2-tile workgroups would outnumber
-// the CUs). Producers stream each chunk into a ring slot of 15 KiB + NW / 2 KiB with
-// wave-wide 1 KiB loads (64 lanes x 16 B):
+// A workgroup covers NW tiles of 16 value columns (NW = 2, or 4 when 2-tile
+// workgroups would outnumber the CUs) with its compute waves, two per tile in the
+// two-wave form or one in the whole-tile form, and two producer waves. Producers
+// stream each chunk into a ring slot of 15 KiB + NW / 2 KiB with wave-wide 1 KiB
+// loads (64 lanes x 16 B):
 //   pieces 0..13  record bytes [0, 14336)          (W, Q~, K^d, T', M)
 //   piece 14      record bytes [14336, 14848) = gamma, lanes 32..63 load it again into [14848, 15360)
 //   then          value tile [16 tokens][16 NW columns] bf16 at kVOff, NW / 2 pieces
@@ -96,12 +97,13 @@ __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const
     }
 }
 
-// Compute waves: NW value tiles x 2 halves of the key dimension. Compute wave
-// (vt, kh) holds rows 64 kh .. 64 kh + 63 of tile vt's 128 x 16 state slice, i.e. the
-// four 16 x 16 accumulator tiles M = 4 kh .. 4 kh + 3. W S, Q~ S and K^d^T Delta all
-// split along those rows, so each chunk costs a wave half the MFMA and VALU work of
-// the whole slice; the two halves of a tile swap their partial W S through LDS at
-// the chunk barrier, and half 1 hands half 0 its partial Q~ S for the output.
+// Compute waves of the two-wave form: NW value tiles x 2 halves of the key
+// dimension. Compute wave (vt, kh) holds rows 64 kh .. 64 kh + 63 of tile vt's
+// 128 x 16 state slice, i.e. the four 16 x 16 accumulator tiles M = 4 kh .. 4 kh + 3.
+// W S, Q~ S and K^d^T Delta all split along those rows, so each chunk costs a wave
+// half the MFMA and VALU work of the whole slice; the two halves of a tile swap their
+// partial W S through LDS at the chunk barrier, and half 1 hands half 0 its partial
+// Q~ S for the output.
 constexpr int kHalves = 2;
 constexpr int kProducers = 2;
 template <int NW>

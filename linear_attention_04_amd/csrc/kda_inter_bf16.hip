@@ -230,11 +230,12 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
 namespace {
 
 // One workgroup per 16 NW value columns of a (sequence, head). While 2-tile
-// workgroups fit one per CU: 2 tiles with an 8-chunk ring (128 KiB + 12 KiB
-// exchange). Beyond that: 4 tiles (8 compute waves, two per SIMD, sharing one record
-// stream) with a 7-chunk ring (119 KiB + 24 KiB), one workgroup per CU at a time.
-// Two 2-tile workgroups per CU (4-chunk rings) were slower: each streams its own copy
-// of the records.
+// workgroups fit one per CU: 2 tiles with an 8-chunk ring (128 KiB, plus a 12 KiB
+// exchange in the two-wave form). Beyond that: 4 tiles sharing one record stream, one
+// workgroup per CU at a time: in the one-wave form, four compute waves (one per SIMD)
+// and an 8-chunk ring (136 KiB); in the two-wave form, eight compute waves (two per
+// SIMD), a 7-chunk ring (119 KiB) and a 24 KiB exchange. Two 2-tile workgroups per CU
+// (4-chunk rings) were slower: each streams its own copy of the records.
 template <bool SAVE, bool OUT>
 hipError_t launch_by_size(const void *v, const int32_t *cu_seqlens, const float *s0, void *out, float *sT,
                           const Geometry &geo, const void *ws, hipStream_t stream) {

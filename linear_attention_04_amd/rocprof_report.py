@@ -15,7 +15,8 @@ hardware pass collects. ``summarize`` turns the CSV files into ``profiles/<mode>
 (per kernel: calls, average / min / max duration, HBM bytes read and written, MFMA
 busy and VALU+MFMA issue share of SIMD cycles) and into
 ``profiles/traffic_<tag>_<workload>.json``. bench.py quotes the latter as measured
-traffic while its recorded source digest matches the kernel sources.
+traffic while its recorded source digest matches the kernel sources (their code;
+comments do not count).
 
 HBM bytes are the counters scaled by what they read for a plain device copy of known
 size (``run --only copy``): FETCH_SIZE counts half the bytes a 128-byte request
@@ -112,11 +113,38 @@ PROFILE_FILES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C++/HIP source without its comments, trailing blanks and empty lines: what the
+    compiler sees. String and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        ch = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif ch in "\"'":
+            j = i + 1
+            while j < n and src[j] != ch:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(ch)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest(names) -> str:
+    """Digest of the code (not the comments) of the named kernel sources."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,6 +36,21 @@ def test_cpu_baseline_object():
     assert cb["value"] > 0 and cb["cores"] >= 1 and isinstance(cb["sample"], str)
 
 
+def test_source_digest_ignores_comments():
+    """A profile's traffic figures stay valid across comment edits of its kernel sources
+    (the compiled code is the same), and not across a change of code."""
+    sys.path.insert(0, ROOT)
+    from linear_attention_04_amd.rocprof_report import code_text
+
+    base = 'int a = 1;\nchar *s = "x // y /* z */";\nchar q = \'"\';\nint b;'
+    edited = ('// header\nint a = 1;  // one\n\n/* a block\n   comment */\nchar *s = "x // y /* z */";\n'
+              'char q = \'"\';   \nint b; /* end */\n')
+    assert code_text(edited).replace(" ", "") == code_text(base).replace(" ", "")
+    assert code_text(base) == base
+    assert code_text(base.replace("1", "2")) != code_text(base)
+    assert code_text('char *s = "a /* b";  // c */ d') == 'char *s = "a /* b";'
+
+
 def _run_bench(*args):
     r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "2", "--no-cpu-baseline", *args],
                        capture_output=True, text=True, timeout=600, cwd=ROOT)
