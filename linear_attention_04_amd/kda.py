@@ -515,3 +515,63 @@ def chunk_prefill_backward_from_saved(q, k, v, g, beta, d_out, workspace, cu_seq
     if st != KDA_OK:
         raise KdaError(st, "kda_backward_token_grad")
     return out
+
+
+_CHUNK_KDA_FN = None
+
+
+def _chunk_kda_function():
+    """The torch.autograd.Function behind :func:`chunk_kda`, made on first use (the
+    module itself imports torch only when a torch-facing function runs)."""
+    global _CHUNK_KDA_FN
+    if _CHUNK_KDA_FN is not None:
+        return _CHUNK_KDA_FN
+    import torch
+
+    class ChunkKDA(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, cu_seqlens, initial_state):
+            out, final_state, ws = chunk_prefill_for_backward(q, k, v, g, beta, cu_seqlens=cu_seqlens,
+                                                              initial_state=initial_state)
+            ctx.save_for_backward(q, k, v, g, beta, cu_seqlens, ws)
+            ctx.has_initial_state = initial_state is not None
+            ctx.set_materialize_grads(False)  # an output outside the loss arrives as None
+            return out, final_state
+
+        @staticmethod
+        def backward(ctx, d_out, d_final_state):
+            q, k, v, g, beta, cu_seqlens, ws = ctx.saved_tensors
+            d_out = torch.zeros_like(v) if d_out is None else d_out.to(v.dtype).contiguous()
+            if d_final_state is not None:
+                d_final_state = d_final_state.to(torch.float32).contiguous()
+            want_ds0 = ctx.has_initial_state and ctx.needs_input_grad[6]
+            grads = chunk_prefill_backward_from_saved(q, k, v, g, beta, d_out, ws, cu_seqlens=cu_seqlens,
+                                                      d_final_state=d_final_state,
+                                                      want_d_initial_state=want_ds0)
+            return (grads["dq"], grads["dk"], grads["dv"], grads["dg"], grads["dbeta"], None,
+                    grads["d_initial_state"] if want_ds0 else None)
+
+    _CHUNK_KDA_FN = ChunkKDA
+    return ChunkKDA
+
+
+def chunk_kda(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=True):
+    """Chunked KDA prefill with torch autograd: returns (out, final_state or None).
+
+    Arguments as :func:`chunk_prefill`. When gradients are wanted (grad mode on and
+    any of q, k, v, g, beta, initial_state requiring them), the forward runs
+    kda_chunk_prefill_for_backward and keeps its backward workspace on the autograd
+    graph; backward() then runs only the reverse pass and the token gradients
+    (:func:`chunk_prefill_backward_from_saved`) and returns dq, dk, dv (bf16), dg,
+    dbeta and the initial state's gradient (fp32). That path is bf16 with K = V = 128;
+    other inputs raise KdaError. Otherwise this is :func:`chunk_prefill`.
+    """
+    import torch
+
+    inputs = (q, k, v, g, beta, initial_state)
+    if torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in inputs):
+        out, final_state = _chunk_kda_function().apply(q, k, v, g, beta, cu_seqlens, initial_state)
+    else:
+        out, final_state = chunk_prefill(q, k, v, g, beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
+                                         final_state=True if output_final_state else None)
+    return out, (final_state if output_final_state else None)
