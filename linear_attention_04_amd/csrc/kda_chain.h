@@ -252,7 +252,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
 template <int KH, int DEPTH, bool SAVE, bool OUT, int NW, class Sync>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
                                              char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
-                                             Sync &sync, char *sdst0 = nullptr) {
+                                             Sync &sync, char *sdst0 = nullptr, size_t sstride = 0) {
     auto slot_of = [&](int64_t j) {
         return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
     };
@@ -269,7 +269,7 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, y, px, py;
         char *xc = xchg_of(j);
-        chunk_part_a<KH, SAVE, OUT>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * kStateBytesBf16 : nullptr);
+        chunk_part_a<KH, SAVE, OUT>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * sstride : nullptr);
         wait_lgkm0();  // the partial products are in LDS before the barrier
         sync.barrier(j + 1);  // B_{j+1}
         read_partner<KH, OUT>(xc, lane, px, py);
@@ -291,13 +291,15 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 // The compute waves' part of a recurrent workgroup: the state slice in, the chunk
 // loop over the LDS ring, the state slice out. Compute wave (vt, kh) owns value
 // columns col0 + 16 vt .. + 15 and key rows 64 kh .. + 63. SAVE: `states` points at
-// the sequence's first chunk in the [H][max_chunks] array of chunk start states.
+// the sequence's first chunk in the [max_chunks][H] array of chunk start states, and
+// `sstride` is the distance between a pair's consecutive chunks there.
 // OUT: the chunk outputs go to `out`. The final state goes to `sT` unless it is NULL.
 template <int DEPTH, bool SAVE, bool OUT, int NW, class Sync>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
-                                             float *__restrict__ sT, Sync &sync, char *states = nullptr) {
+                                             float *__restrict__ sT, Sync &sync, char *states = nullptr,
+                                             size_t sstride = 0) {
     const int c = lane & 15, grp = lane >> 4;
     const int vt = wid >> 1, kh = wid & 1;
     lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
@@ -322,9 +324,11 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile
     char *sdst0 = SAVE ? states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16 : nullptr;
     if (kh == 0)
-        compute_wave<0, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0);
+        compute_wave<0, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0,
+                                              sstride);
     else
-        compute_wave<1, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0);
+        compute_wave<1, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0,
+                                              sstride);
 
     if (sT) {
 #pragma unroll

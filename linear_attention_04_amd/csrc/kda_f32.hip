@@ -40,7 +40,7 @@ __global__ __launch_bounds__(64) void kda_intra_f32_kernel(
     int len;
     chunk_span(cu, chunk_off, chunk_seq, chunk, T, N, max_chunks, start, len);
     if (len == 0) return;
-    float *rec = records + ((size_t)h * max_chunks + chunk) * F32Rec<K>::FLOATS;  // head-major
+    float *rec = records + ((size_t)chunk * H + h) * F32Rec<K>::FLOATS;  // chunk-major
 
     for (int idx = tid; idx < 16 * K; idx += 64) {
         const int r = idx / K, ch = idx % K;
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(K) void kda_inter_f32_kernel(
         const int64_t tok0 = sc.tok_begin + 16 * (ci - sc.chunk_begin);
         const int64_t rem = sc.tok_end - tok0;
         const int len = rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
-        const float *rec = records + ((size_t)h * max_chunks + ci) * F32Rec<K>::FLOATS;
+        const float *rec = records + ((size_t)ci * H + h) * F32Rec<K>::FLOATS;
         __syncthreads();
         for (int idx = j; idx < F32Rec<K>::FLOATS; idx += V) R[idx] = rec[idx];
         __syncthreads();

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     const int64_t tok = start + c;
     const size_t krow = ((size_t)(row_ok ? tok : start) * H + h) * KD;  // q, k, g, dq, dk, dg row of token c
     const size_t vrow = ((size_t)(row_ok ? tok : start) * H + h) * VD;  // v, d_out, dv row
-    const size_t hc = (size_t)h * max_chunks + chunk;
+    const size_t hc = (size_t)chunk * H + h;  // chunk-major, like the records
     const char *S0 = states + hc * kStateBytesBf16 + lane * 16;
     const char *Rs = dstates + hc * kStateBytesBf16 + lane * 16;
     const float b = row_ok ? beta[(size_t)tok * H + h] : 0.f;

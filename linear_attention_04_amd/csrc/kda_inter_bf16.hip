@@ -39,7 +39,7 @@
 namespace kda {
 namespace {
 
-// SAVE: every chunk's start state goes to `states` ([H][max_chunks] x 32 KiB
+// SAVE: every chunk's start state goes to `states` ([max_chunks][H] x 32 KiB
 // fragments), for a backward pass. OUT: the output is written (a recomputed forward
 // that only saves states writes neither output nor final state). FULL: one compute
 // wave per tile (compute_role_full) instead of two (compute_role); the prefill's form.
@@ -84,7 +84,11 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
     if (wid >= inter_compute_waves<NW, FULL>()) {
         // ---- producer ----
         const int p = wid - inter_compute_waves<NW, FULL>();
-        const char *rec0 = records + ((size_t)h * max_chunks + sc.chunk_begin) * kRecBytesBf16;  // head-major
+        // records are chunk-major: a chunk's records for all heads are contiguous, so the
+        // workgroups in flight, which move through the chunks at about the same pace, read
+        // one region of HBM (and K1's workgroups in flight write one)
+        const char *rec0 = records + ((size_t)sc.chunk_begin * H + h) * kRecBytesBf16;
+        const size_t rec_stride = (size_t)H * kRecBytesBf16;
         const char *v0 = reinterpret_cast<const char *>(v) + tok_bytes;
         auto len_of = [&](int64_t j) {
             const int64_t rem = sc.tok_end - (sc.tok_begin + 16 * j);
@@ -93,7 +97,7 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
         auto issue = [&](int64_t j) {
             const unsigned int slot =
                 (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
-            issue_chunk<NW>(ring, slot, rec0 + (size_t)j * kRecBytesBf16, v0 + (size_t)j * chunk_rows, len_of(j), p,
+            issue_chunk<NW>(ring, slot, rec0 + (size_t)j * rec_stride, v0 + (size_t)j * chunk_rows, len_of(j), p,
                             lo);
         };
         for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
@@ -121,9 +125,11 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
                                           OUT ? sT : nullptr, sync);
         return;
     }
-    char *st = SAVE ? states + ((size_t)h * max_chunks + sc.chunk_begin) * kStateBytesBf16 : nullptr;
+    // chunk start states, chunk-major like the records: chunk j of this pair is H states on
+    char *st = SAVE ? states + ((size_t)sc.chunk_begin * H + h) * kStateBytesBf16 : nullptr;
+    const size_t sstride = (size_t)H * kStateBytesBf16;
     compute_role<DEPTH, SAVE, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
-                                       OUT ? sT : nullptr, sync, st);
+                                       OUT ? sT : nullptr, sync, st, sstride);
 }
 
 template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>

@@ -60,11 +60,11 @@ struct Geometry {
     int64_t max_chunks;      // upper bound on chunks over all sequences
     size_t off_chunk_off;    // int32 [N + 1]
     size_t off_chunk_seq;    // int32 [max_chunks]
-    size_t off_records;      // records [H][max_chunks] (head-major: a head's chunks are contiguous)
+    size_t off_records;      // records [max_chunks][H] (chunk-major: a chunk's heads are contiguous)
     size_t record_bytes;
     size_t total_bytes;
     // backward only (make_backward_geometry): backward records, chunk start states
-    // and chunk end-state gradients, each [H][max_chunks] like the records
+    // and chunk end-state gradients, each [max_chunks][H] like the records
     size_t off_brecords;
     size_t off_states;
     size_t off_dstates;

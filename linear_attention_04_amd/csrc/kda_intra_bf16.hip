@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// BWD: also each chunk's backward record, to `brecords` ([H][max_chunks] like the records).
+// BWD: also each chunk's backward record, to `brecords` ([max_chunks][H] like the records).
 template <bool SCALAR_GATE, bool BWD>
 __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
@@ -37,8 +37,8 @@ __global__ __launch_bounds__(64 * kWaves) void kda_intra_bf16_kernel(
     int len;
     chunk_span(cu, chunk_off, chunk_seq, chunk, T, N, max_chunks, start, len);
     if (len == 0) return;  // same chunk for the whole workgroup
-    char *rec = records + ((size_t)h * max_chunks + chunk) * kRecBytesBf16;  // head-major
-    char *brec = BWD ? brecords + ((size_t)h * max_chunks + chunk) * kBRecBytes : nullptr;
+    char *rec = records + ((size_t)chunk * H + h) * kRecBytesBf16;  // chunk-major
+    char *brec = BWD ? brecords + ((size_t)chunk * H + h) * kBRecBytes : nullptr;  // chunk-major
     intra::chunk_record<SCALAR_GATE, BWD>(q, k, g, beta, start, len, h, H, head_ok, lds[wave], rec, lane, brec);
 }
 

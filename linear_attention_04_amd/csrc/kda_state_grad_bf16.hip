@@ -175,10 +175,10 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&R)[4], co
 // The chunk loop of compute wave (vt, KH): barrier B_j (j = 0 .. nchunks) as in the
 // forward recurrent kernel, with the chunks taken last to first (step j works on
 // chunk nchunks - 1 - j). rdst0 points at this lane's fragment of the sequence's first
-// chunk in the end-state gradient array.
+// chunk in the end-state gradient array, and consecutive chunks are rstride bytes apart.
 template <int KH, int DEPTH, int NW>
 __device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t nchunks, int vt, int lane,
-                                             char *rdst0) {
+                                             char *rdst0, size_t rstride) {
     auto slot_of = [&](int64_t j) {
         return ring + (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
     };
@@ -188,7 +188,7 @@ __device__ __forceinline__ void compute_wave(f32x4 (&R)[4], char *ring, int64_t 
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, px;
         char *xc = xchg_of(j);
-        chunk_part_a<KH>(cur, R, x, xc, lane, rdst0 + (size_t)(nchunks - 1 - j) * kStateBytesBf16);
+        chunk_part_a<KH>(cur, R, x, xc, lane, rdst0 + (size_t)(nchunks - 1 - j) * rstride);
         wait_lgkm0();  // the partial X is in LDS before the barrier
         barrier();     // B_{j+1}
         px = *reinterpret_cast<const f32x4 *>(xc + (1 - KH) * 1024 + lane * 16);
@@ -224,7 +224,9 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
     const int col0 = vg * NW * 16;
     const SeqChunks sc = seq_chunks(cu, chunk_off, n, T, max_chunks);
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
-    const size_t head_chunk0 = (size_t)h * max_chunks + sc.chunk_begin;  // [H][max_chunks] index of chunk 0
+    // backward records and end-state gradients are chunk-major ([max_chunks][H]): this
+    // pair's chunk c sits H entries after its chunk c - 1
+    const size_t head_chunk0 = (size_t)sc.chunk_begin * H + h;  // index of chunk 0
 
     if (wid >= compute_waves<NW>()) {
         // ---- producer: chunk nchunks - 1 - j into slot j % DEPTH ----
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
             const int len = rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
             const unsigned int slot =
                 (unsigned int)__builtin_amdgcn_readfirstlane((int)(j % DEPTH) * slot_bytes<NW>());
-            issue_chunk<NW>(ring, slot, rec0 + (size_t)c * kBRecBytes, d0 + (size_t)c * chunk_rows, len, p, lo);
+            issue_chunk<NW>(ring, slot, rec0 + (size_t)c * H * kBRecBytes, d0 + (size_t)c * chunk_rows, len, p, lo);
         };
         for (int64_t j = 0; j < DEPTH - 1 && j < nchunks; ++j) issue(j);
         for (int64_t j = 0; j < nchunks; ++j) {
@@ -282,9 +284,9 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
     char *rdst0 = dstates + head_chunk0 * kStateBytesBf16 +
                   ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16;
     if (kh == 0)
-        compute_wave<0, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0);
+        compute_wave<0, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0, (size_t)H * kStateBytesBf16);
     else
-        compute_wave<1, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0);
+        compute_wave<1, DEPTH, NW>(R, ring, nchunks, vt, lane, rdst0, (size_t)H * kStateBytesBf16);
     if (ds0) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)

@@ -62,7 +62,7 @@ def test_backward_small_with_intermediates():
         r = reference.chunked_backward(x["q"][:, h], x["k"][:, h], x["v"][:, h], x["g"][:, h], x["beta"][:, h],
                                        d_out[:, h], x["initial_state"][0, h], d_fs[0, h], intermediates=True)
         for ci in range(4):
-            o = (h * lay["max_chunks"] + ci) * 32768
+            o = (ci * w.heads + h) * 32768  # [chunk][head]
             s0 = gu.decode_state_fragments(raw[lay["off_states"] + o:lay["off_states"] + o + 32768])
             rr = gu.decode_state_fragments(raw[lay["off_dstates"] + o:lay["off_dstates"] + o + 32768])
             gu.assert_close_rel(f"S0[h{h},c{ci}]", s0, r["S0s"][ci])

@@ -189,7 +189,7 @@ def test_intra_chunk_intermediates_match_chunked_reference():
         _, _, inter = reference.chunked(x["q"][:, h], x["k"][:, h], x["v"][:, h], x["g"][:, h],
                                         x["beta"][:, h], None, intermediates=True)
         for ci, it in enumerate(inter):
-            rec = raw[off + (h * n_chunks + ci) * 14848: off + (h * n_chunks + ci + 1) * 14848]
+            rec = raw[off + (ci * H + h) * 14848: off + (ci * H + h + 1) * 14848]  # [chunk][head]
             n = it["W"].shape[0]
             beta_c = x["beta"][16 * ci:16 * ci + n, h].astype(np.float64)
             tp_ref = it["T"] * beta_c[None, :]
