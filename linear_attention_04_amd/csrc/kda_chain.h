@@ -309,7 +309,7 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)key_of(m, 4 * grp + i) * VD];
     } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -334,7 +334,7 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
+            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)key_of(m, 4 * grp + i) * VD] = S[m][i];
     }
 }
 
@@ -495,7 +495,7 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+            for (int i = 0; i < 4; ++i) S[m][i] = s0[sbase + (size_t)key_of(m, 4 * grp + i) * VD];
     } else {
 #pragma unroll
         for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -508,7 +508,7 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = S[m][i];
+            for (int i = 0; i < 4; ++i) sT[sbase + (size_t)key_of(m, 4 * grp + i) * VD] = S[m][i];
     }
 }
 

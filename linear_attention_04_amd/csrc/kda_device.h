@@ -17,6 +17,17 @@
 
 namespace kda {
 
+// The key (channel) order the kernels share. In the row layout (lane = token c), element
+// e of lane group grp holds channel chan_of(e, grp): eight consecutive channels per
+// 16-byte load of a bf16 row. Row r of 16 x 16 accumulator tile m of a 128-key state
+// slice holds key key_of(m, r). The two agree, key_of(m, 4 grp + i) = chan_of(4 m + i,
+// grp), so a state tile in the accumulator layout, rounded to bf16, pairs key by key
+// with row-layout operands in a 16x16x32 product (elements 8s .. 8s + 7 = tiles 2s, 2s + 1).
+__host__ __device__ constexpr int chan_of(int e, int grp) { return 32 * (e >> 3) + 8 * grp + (e & 7); }
+__host__ __device__ constexpr int key_of(int m, int r) {
+    return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -34,7 +34,8 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // over all 128 channels (this lane's 32 channels, then summed over the four lane
 // groups). Lane (c, 0) writes them to rows c of `a_rows` and `p_rows` (row-major
 // 16 x 16 in LDS). Columns i > c are written as 0. The lane holds token c, channels
-// 16j + 4grp + e (element 4j + e) of k, q and the running gate.
+// chan_of(e, grp) (element e) of k, q and the running gate; the sums do not depend on
+// which channels a lane holds.
 __device__ __forceinline__ void exact_pair_rows(const float (&kr)[32], const float (&qr)[32], const float (&G)[32],
                                                 int lane, float *a_rows, float *p_rows) {
     const int c = lane & 15, grp = lane >> 4, base = lane & 48;

@@ -18,8 +18,10 @@
 // G_C's gradient (through K^d and gamma) added at the last token.
 //
 // Layouts. "Row layout": lane (c, grp) = (lane % 16, lane / 16) holds token c and
-// channels 16j + 4grp + i (element 4j + i); "slab" s of it is j = 2s, 2s + 1 (eight
-// bf16, the 16x16x32 operand that matches the state fragments' key order). Products
+// channels chan_of(e, grp) = 32s + 8grp + u (element e = 8s + u, kda_device.h); "slab" s
+// of it is elements 8s .. 8s + 7 (eight bf16, the 16x16x32 operand that matches the
+// state fragments' key order), and "key tile" kt is elements 4kt .. 4kt + 3, keys
+// key_of(kt, 4grp + i) = rows 4grp + i of accumulator tile kt. Products
 // over the 128 keys take the state fragments as stored. Products over the 128 value
 // columns need the state with keys across lanes: half of a fragment (16 keys x 16
 // columns) taken as a 16x16x16 operand and multiplied by the identity comes out with
@@ -166,26 +168,33 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     {
         float kr[32], qr[32], G[32];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint2 qw = make_uint2(0u, 0u), kw = make_uint2(0u, 0u);
-            float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < 4; ++s) {  // channels 32s + 8grp .. + 7: one 16-byte load of q and of k
+            uint4 qw = make_uint4(0u, 0u, 0u, 0u), kw = make_uint4(0u, 0u, 0u, 0u);
+            float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
             if (row_ok) {
-                qw = *reinterpret_cast<const uint2 *>(q + krow + 16 * j + 4 * grp);
-                kw = *reinterpret_cast<const uint2 *>(k + krow + 16 * j + 4 * grp);
-                if (!SCALAR_GATE) gv = *reinterpret_cast<const float4 *>(g + krow + 16 * j + 4 * grp);
+                qw = *reinterpret_cast<const uint4 *>(q + krow + 32 * s + 8 * grp);
+                kw = *reinterpret_cast<const uint4 *>(k + krow + 32 * s + 8 * grp);
+                if (!SCALAR_GATE) {
+                    g0 = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp);
+                    g1 = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp + 4);
+                }
             }
-            qr[4 * j] = __uint_as_float(qw.x << 16);
-            qr[4 * j + 1] = __uint_as_float(qw.x & 0xffff0000u);
-            qr[4 * j + 2] = __uint_as_float(qw.y << 16);
-            qr[4 * j + 3] = __uint_as_float(qw.y & 0xffff0000u);
-            kr[4 * j] = __uint_as_float(kw.x << 16);
-            kr[4 * j + 1] = __uint_as_float(kw.x & 0xffff0000u);
-            kr[4 * j + 2] = __uint_as_float(kw.y << 16);
-            kr[4 * j + 3] = __uint_as_float(kw.y & 0xffff0000u);
-            G[4 * j] = gv.x;
-            G[4 * j + 1] = gv.y;
-            G[4 * j + 2] = gv.z;
-            G[4 * j + 3] = gv.w;
+            const unsigned int qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qr[8 * s + 2 * i] = __uint_as_float(qa[i] << 16);
+                qr[8 * s + 2 * i + 1] = __uint_as_float(qa[i] & 0xffff0000u);
+                kr[8 * s + 2 * i] = __uint_as_float(ka[i] << 16);
+                kr[8 * s + 2 * i + 1] = __uint_as_float(ka[i] & 0xffff0000u);
+            }
+            G[8 * s] = g0.x;
+            G[8 * s + 1] = g0.y;
+            G[8 * s + 2] = g0.z;
+            G[8 * s + 3] = g0.w;
+            G[8 * s + 4] = g1.x;
+            G[8 * s + 5] = g1.y;
+            G[8 * s + 6] = g1.z;
+            G[8 * s + 7] = g1.w;
         }
         if (SCALAR_GATE) {
             const float gs = row_inclusive_sum(row_ok ? g[(size_t)tok * H + h] : 0.f);
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     // slabs) serve the products over the keys as stored and, moved across lanes by the
     // selection MFMAs, this tile's share of the products over the values.
     f32x4 dpa = zero4(), dtpa = zero4();  // dP[4grp + i][c], dT'[4grp + i][c]
-    f32x4 dqp[8], dkp[8], dkd[8];         // (dO S0^T)^T, (dU S0^T)^T, (Delta R^T)^T: token c, keys 16kt + 4grp + i
-    float dgam[8];                        // key 16kt + c, summed over this lane group's columns
+    f32x4 dqp[8], dkp[8], dkd[8];         // (dO S0^T)^T, (dU S0^T)^T, (Delta R^T)^T: token c, keys key_of(kt, 4grp + i)
+    float dgam[8];                        // key key_of(kt, c), summed over this lane group's columns
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
         dqp[kt] = dkp[kt] = dkd[kt] = zero4();
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         // products over this tile's 16 columns, for all 128 keys
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            // key 16kt + c across lanes, columns 16vt + 4grp + i: the fragment's half
+            // key key_of(kt, c) across lanes, columns 16vt + 4grp + i: the fragment's half
             // (kt & 1) as a 16x16x16 operand (rows: columns of S), times the identity
             const f32x4 st = mfma_16x16x16(half4(s0f[kt >> 1], kt & 1), I4, zero4());
             const f32x4 rt = mfma_16x16x16(half4(rf[kt >> 1], kt & 1), I4, zero4());
@@ -394,11 +403,12 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
                                                      16, off, 0, 0, 0);
         }
     }
-    float4 gk[8];  // g of token c, channels 16kt + 4grp .. + 3
+    float4 gk[8];  // g of token c, channels key_of(kt, 4grp) .. + 3
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
         gk[kt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (!SCALAR_GATE && row_ok) gk[kt] = *reinterpret_cast<const float4 *>(g + krow + 16 * kt + 4 * grp);
+        if (!SCALAR_GATE && row_ok)
+            gk[kt] = *reinterpret_cast<const float4 *>(g + krow + key_of(kt, 4 * grp));
     }
 
     // ================= 3. the 16 x 16 backward =================
@@ -478,8 +488,8 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     // so the products of A~ and P with the gates are differentiated pair by pair.
     auto key_tile = [&](int kt, auto exact_tag) {
         constexpr bool EXACT = decltype(exact_tag)::value;
-        const int cb = 2 * (16 * kt + 4 * grp);  // byte of channel 16kt + 4grp in a bf16 row
-        // channels 16kt + 4grp + i of token c
+        const int cb = 2 * key_of(kt, 4 * grp);  // byte of channel key_of(kt, 4grp) in a bf16 row
+        // channels key_of(kt, 4grp) + i of token c
         const f32x4 kk = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(tk + tile_off<256>(c, cb)));
         const f32x4 qq = bf16x4_to_f32(*reinterpret_cast<const bf16x4 *>(tq + tile_off<256>(c, cb)));
         f32x4 G;
@@ -562,7 +572,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
         }
 
         // dgamma for this lane's four channels: sum over the lane groups, then
-        // channel 16kt + 4grp + i sits in lane 4grp + i
+        // channel key_of(kt, 4grp + i) sits in lane 4grp + i
         float dgt = dgam[kt];
         dgt += __shfl_xor(dgt, 16, 64);
         dgt += __shfl_xor(dgt, 32, 64);

@@ -19,7 +19,8 @@
 //   Delta = U - W S                   (S rounded to bf16 as the MFMA operand)
 //   O     = Q~ S + M V                -> out (bf16)
 //   S     = Diag(gamma) S + K^d^T Delta   (two-term bf16 split of Delta)
-// The accumulator layout of S (lane: rows 4grp + i of column c) is, after rounding
+// The accumulator layout of S (lane: rows 4grp + i of column c, row r of tile m being key
+// key_of(m, r)) is, after rounding
 // to bf16, directly the B operand of W S and Q~ S, because the intra-chunk kernel
 // stores W and Q~ with matching channel order; Delta's accumulator layout is the B
 // operand of K^d^T Delta. Across lanes, only gamma moves (DPP broadcasts inside

@@ -67,12 +67,15 @@ __device__ __forceinline__ void rec_store(char *p, const T &v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 
-__device__ __forceinline__ void load_bf16x4(const __bf16 *p, float *dst) {
-    const uint2 raw = *reinterpret_cast<const uint2 *>(p);
-    dst[0] = __uint_as_float(raw.x << 16);
-    dst[1] = __uint_as_float(raw.x & 0xffff0000u);
-    dst[2] = __uint_as_float(raw.y << 16);
-    dst[3] = __uint_as_float(raw.y & 0xffff0000u);
+// Eight consecutive bf16 values (one 16-byte load) as fp32.
+__device__ __forceinline__ void load_bf16x8(const __bf16 *p, float *dst) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(p);
+    const unsigned int w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dst[2 * i] = __uint_as_float(w[i] << 16);
+        dst[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
 }
 
 // The record of chunk [start, start + len) of head h (len in 1..16), written to
@@ -91,26 +94,30 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     const int c = lane & 15;
     const int grp = lane >> 4;
 
-    // ---- load: lane holds token c, channels 16j + 4grp + i (element e = 4j + i) ----
+    // ---- load: lane holds token c, channels chan_of(e, grp) = 32s + 8grp + u (element
+    // e = 8s + u): one 16-byte load of q and of k per s ----
     const bool row_ok = c < len;
     const int64_t t = start + c;
     float kr[32], qr[32], gr[32];
-    const size_t rowoff = ((size_t)(row_ok ? t : start) * H + h) * KD + 4 * grp;
+    const size_t rowoff = ((size_t)(row_ok ? t : start) * H + h) * KD + 8 * grp;
     const float gs = (SCALAR_GATE && row_ok) ? g[(size_t)t * H + h] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int s = 0; s < 4; ++s) {
         if (row_ok) {
-            load_bf16x4(q + rowoff + 16 * j, qr + 4 * j);
-            load_bf16x4(k + rowoff + 16 * j, kr + 4 * j);
+            load_bf16x8(q + rowoff + 32 * s, qr + 8 * s);
+            load_bf16x8(k + rowoff + 32 * s, kr + 8 * s);
             if (SCALAR_GATE) {
-                gr[4 * j] = gr[4 * j + 1] = gr[4 * j + 2] = gr[4 * j + 3] = gs;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) gr[8 * s + u] = gs;
             } else {
-                const float4 gv = *reinterpret_cast<const float4 *>(g + rowoff + 16 * j);
-                gr[4 * j] = gv.x; gr[4 * j + 1] = gv.y; gr[4 * j + 2] = gv.z; gr[4 * j + 3] = gv.w;
+                const float4 g0 = *reinterpret_cast<const float4 *>(g + rowoff + 32 * s);
+                const float4 g1 = *reinterpret_cast<const float4 *>(g + rowoff + 32 * s + 4);
+                gr[8 * s] = g0.x; gr[8 * s + 1] = g0.y; gr[8 * s + 2] = g0.z; gr[8 * s + 3] = g0.w;
+                gr[8 * s + 4] = g1.x; gr[8 * s + 5] = g1.y; gr[8 * s + 6] = g1.z; gr[8 * s + 7] = g1.w;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { qr[4 * j + i] = 0.f; kr[4 * j + i] = 0.f; gr[4 * j + i] = 0.f; }
+            for (int u = 0; u < 8; ++u) { qr[8 * s + u] = 0.f; kr[8 * s + u] = 0.f; gr[8 * s + u] = 0.f; }
         }
     }
     const float b = row_ok ? beta[(size_t)t * H + h] : 0.f;
@@ -136,7 +143,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
             span = fmaxf(span, fmaxf(fabsf(d0), fabsf(d1)));
             const float up0 = __expf(d0), up1 = __expf(d1);
             const float dn0 = __expf(-d0), dn1 = __expf(-d1);
-            const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);  // channel of e; e + 1 is ch + 1
+            const int ch = chan_of(e, grp);  // channel of e; e + 1 is ch + 1
             const __bf16 kd0 = to_bf16(kr[e] * (dn0 * row_bcast<15>(up0)));
             const __bf16 kd1 = to_bf16(kr[e + 1] * (dn1 * row_bcast<15>(up1)));
             L.kd[ch * kChStride + c] = kd0;
@@ -163,7 +170,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         acc_p = mfma_16x16x32(vqhh, vkbh, acc_p);
         acc_p = mfma_16x16x32(vqhl, vkbh, acc_p);
         acc_p = mfma_16x16x32(vqhh, vkbl, acc_p);
-        if (BWD && head_ok)  // K^d in the W layout: token c, channels 16j + 4grp + i
+        if (BWD && head_ok)  // K^d in the W layout: token c, channels chan_of(8s + u, grp)
             *reinterpret_cast<uint4 *>(brec + kBRecKD + (s * 64 + lane) * 16) =
                 make_uint4(kdr[0], kdr[1], kdr[2], kdr[3]);
     }
@@ -179,7 +186,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = 8 * s + 2 * u;
-                const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);
+                const int ch = chan_of(e, grp);
                 const __bf16 kd0 = to_bf16(kr[e] * __expf(row_bcast<15>(G[e]) - G[e]));
                 const __bf16 kd1 = to_bf16(kr[e + 1] * __expf(row_bcast<15>(G[e + 1]) - G[e + 1]));
                 L.kd[ch * kChStride + c] = kd0;
@@ -202,12 +209,14 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     }
 
     wave_sync();
-    // K^d to the record now, so that its LDS area is free for A and K+
+    // K^d to the record now, so that its LDS area is free for A and K+: tile pair mp,
+    // lane (c, grp) holds keys key_of(2mp, c) (low 8 bytes) and key_of(2mp + 1, c),
+    // tokens 4grp .. + 3
     if (head_ok) {
 #pragma unroll
         for (int mp = 0; mp < 4; ++mp) {
-            const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + c) * kChStride + 4 * grp]);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[(32 * mp + 16 + c) * kChStride + 4 * grp]);
+            const uint2 lo = *reinterpret_cast<const uint2 *>(&L.kd[key_of(2 * mp, c) * kChStride + 4 * grp]);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(&L.kd[key_of(2 * mp + 1, c) * kChStride + 4 * grp]);
             rec_store(rec + kRecKD + (mp * 64 + lane) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
     }
@@ -242,7 +251,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     // exp(G_C) is token 15's exp(G), broadcast ----
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        const int ch = 16 * (e >> 2) + 4 * grp + (e & 3);
+        const int ch = chan_of(e, grp);
         const float ep = __expf(G[e]);
         L.kp[ch * kChStride + c] = kr[e] * ep;
         qr[e] *= ep;
@@ -274,12 +283,14 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         mml2[i] = mml2[4 + i] = mml[i];
     }
 
-    // ---- W^T = K+^T T'^T and (M K+)^T = K+^T M^T, tile by tile of 16 channels.
+    // ---- W^T = K+^T T'^T and (M K+)^T = K+^T M^T, tile by tile of 16 channels: tile jt
+    // holds keys key_of(jt, 0 .. 15), so its outputs land on elements 4jt .. + 3 of the
+    // row layout.
     // A operand [K+_hi | K+_lo]: ([K+_hi | K+_lo] . [X; X]) = (K+_hi + K+_lo) X. ----
     bf16x8 wv[4], qv[4];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) {
-        const f32x4 kpt = *reinterpret_cast<const f32x4 *>(&L.kp[(16 * jt + c) * kChStride + 4 * grp]);
+        const f32x4 kpt = *reinterpret_cast<const f32x4 *>(&L.kp[key_of(jt, c) * kChStride + 4 * grp]);
         bf16x4 kph, kpl;
         split_bf16x4(kpt, kph, kpl);
         bf16x8 kp2;
@@ -314,15 +325,15 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     *reinterpret_cast<bf16x8 *>(rec + kRecTB + lane * 16) = tbv;
     *reinterpret_cast<bf16x8 *>(rec + kRecMM + lane * 16) = mmv;
     if (c < 8) {
-        // gamma_perm[grp][4c + i] = gamma[16c + 4grp + i]
-        const float4 gv = *reinterpret_cast<const float4 *>(&L.gam[16 * c + 4 * grp]);
+        // gamma_perm[grp][4c + i] = gamma[key_of(c, 4grp + i)]: accumulator tile c, row 4grp + i
+        const float4 gv = *reinterpret_cast<const float4 *>(&L.gam[key_of(c, 4 * grp)]);
         *reinterpret_cast<float4 *>(rec + kRecGAM + (grp * 32 + 4 * c) * 4) = gv;
         if (BWD) *reinterpret_cast<float4 *>(brec + kBRecGAM + (grp * 32 + 4 * c) * 4) = gv;
     }
     if (BWD) {
         // W and Q~ channel-major through the K+ area (its last reads were above),
-        // then read back in the K^d layout: lane (c, grp), pair mp holds channel
-        // 32 mp + c (low 8 bytes) and 32 mp + 16 + c (high 8 bytes), tokens 4grp .. + 3
+        // then read back in the K^d layout: lane (c, grp), pair mp holds key
+        // key_of(2mp, c) (low 8 bytes) and key_of(2mp + 1, c) (high 8 bytes), tokens 4grp .. + 3
         wave_sync();
         __bf16 *tw = reinterpret_cast<__bf16 *>(L.kp);
         __bf16 *tq = tw + KD * kChStride;
@@ -330,7 +341,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         for (int jt = 0; jt < 8; ++jt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int ch = 16 * jt + 4 * grp + i;
+                const int ch = key_of(jt, 4 * grp + i);
                 tw[ch * kChStride + c] = wv[jt >> 1][4 * (jt & 1) + i];
                 tq[ch * kChStride + c] = qv[jt >> 1][4 * (jt & 1) + i];
             }
@@ -338,7 +349,7 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
         wave_sync();
 #pragma unroll
         for (int mp = 0; mp < 4; ++mp) {
-            const int lo = (32 * mp + c) * kChStride + 4 * grp, hi = (32 * mp + 16 + c) * kChStride + 4 * grp;
+            const int lo = key_of(2 * mp, c) * kChStride + 4 * grp, hi = key_of(2 * mp + 1, c) * kChStride + 4 * grp;
             const uint2 wl = *reinterpret_cast<const uint2 *>(&tw[lo]), wh = *reinterpret_cast<const uint2 *>(&tw[hi]);
             const uint2 ql = *reinterpret_cast<const uint2 *>(&tq[lo]), qh = *reinterpret_cast<const uint2 *>(&tq[hi]);
             *reinterpret_cast<uint4 *>(brec + kBRecWT + (mp * 64 + lane) * 16) = make_uint4(wl.x, wl.y, wh.x, wh.y);

@@ -92,7 +92,7 @@ __device__ __forceinline__ void issue_chunk(char *ring, unsigned int slot, const
 
 // One chunk's operands for one half (rows 64 KH .. 64 KH + 63 of a tile).
 struct HalfOps {
-    bf16x8 kd[2];  // K^d slabs 2 KH, 2 KH + 1 (token c, keys 32s + 4grp + i, 32s + 16 + 4grp + i)
+    bf16x8 kd[2];  // K^d slabs 2 KH, 2 KH + 1 (token c, keys chan_of(8s + u, grp))
     bf16x8 wt[4];  // W^T tiles 4 KH .. + 3, tokens 4grp .. + 3 twice (both halves of the reduction)
     s16x4 qt[4];   // Q~^T tiles 4 KH .. + 3, tokens 4grp .. + 3
     float2 gam;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R[m][i] = dsT[sbase + (size_t)(16 * m + 4 * grp + i) * VD];
+            for (int i = 0; i < 4; ++i) R[m][i] = dsT[sbase + (size_t)key_of(m, 4 * grp + i) * VD];
     } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) R[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * waves<NW>()) void kda_state_grad_bf16_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ds0[sbase + (size_t)(16 * m + 4 * grp + i) * VD] = R[m][i];
+            for (int i = 0; i < 4; ++i) ds0[sbase + (size_t)key_of(m, 4 * grp + i) * VD] = R[m][i];
     }
 }
 

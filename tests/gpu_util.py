@@ -184,7 +184,7 @@ def backward_workspace_layout(T, H, N):
 def decode_state_fragments(raw: np.ndarray) -> np.ndarray:
     """A 128 x 128 bf16 state in fragment layout (32768 bytes) -> [key][value] fp64:
     fragment (ct, ks), lane (c, grp), element e holds value column 16 ct + c and key
-    32 ks + 4 grp + e (e < 4) or 32 ks + 16 + 4 grp + e - 4."""
+    32 ks + 8 grp + e."""
     u16 = np.frombuffer(np.ascontiguousarray(raw).tobytes(), dtype=np.uint16).reshape(8, 4, 64, 8)
     vals = (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     out = np.empty((128, 128))
@@ -193,7 +193,7 @@ def decode_state_fragments(raw: np.ndarray) -> np.ndarray:
     for ct in range(8):
         for ks in range(4):
             for e in range(8):
-                key = 32 * ks + (4 * grp + e if e < 4 else 16 + 4 * grp + e - 4)
+                key = 32 * ks + 8 * grp + e
                 out[key, 16 * ct + c] = vals[ct, ks, :, e]
     return out
 

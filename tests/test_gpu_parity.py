@@ -199,13 +199,18 @@ def test_intra_chunk_intermediates_match_chunked_reference():
             def bf(u16):
                 return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
+            # the kernels' key order: row-layout element 8s + u of lane group g is
+            # channel 32s + 8g + u; row r of accumulator tile m is key
+            # 32(m // 2) + 8(r // 4) + 4(m % 2) + r % 4
+            def key_of(m, r):
+                return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3)
+
             def dec_rowlayout(base):
                 a = bf(rec[base:base + 4096].view(np.uint16).reshape(4, 64, 8))
                 out = np.zeros((16, 128))
                 for s in range(4):
                     for u in range(8):
-                        e = 8 * s + u
-                        out[cl, 16 * (e >> 2) + 4 * gl + (e & 3)] = a[s, :, u]
+                        out[cl, 32 * s + 8 * gl + u] = a[s, :, u]
                 return out
 
             def dec_tile_pairs(base):
@@ -214,7 +219,7 @@ def test_intra_chunk_intermediates_match_chunked_reference():
                 for mp in range(4):
                     for u in range(8):
                         m = 2 * mp + (u >> 2)
-                        out[4 * gl + (u & 3), 16 * m + cl] = a[mp, :, u]
+                        out[4 * gl + (u & 3), key_of(m, cl)] = a[mp, :, u]
                 return out
 
             def dec_hilo(base):
@@ -228,7 +233,7 @@ def test_intra_chunk_intermediates_match_chunked_reference():
             gam_full = np.zeros(128)
             for gg in range(4):
                 for e in range(32):
-                    gam_full[16 * (e >> 2) + 4 * gg + (e & 3)] = gam[gg, e]
+                    gam_full[key_of(e >> 2, 4 * gg + (e & 3))] = gam[gg, e]
             got = {"W": dec_rowlayout(0), "QT": dec_rowlayout(4096), "KD": dec_tile_pairs(8192),
                    "TB": dec_hilo(12288), "MM": dec_hilo(13312)}
             ref = {"W": it["W"], "QT": qt_ref, "KD": it["Kd"], "TB": tp_ref, "MM": m_ref}
