@@ -13,13 +13,17 @@ constexpr int kChunk = 16;
 constexpr int kMaxSeqs = 1 << 20;  // packed sequences per call
 
 // bf16 K = V = 128 record of one (chunk, head), written by the intra-chunk kernel and
-// read by the inter-chunk kernel. Byte offsets:
-//   W    0      [4 slabs][64 lanes][8 bf16]  W = T' K+ in 16x16x32 A-operand layout
+// read by the inter-chunk kernel. Keys follow chan_of / key_of (kda_device.h). Byte offsets:
+//   W    0      [4 slabs][64 lanes][8 bf16]  W = T' K+ in 16x16x32 A-operand layout: slab s,
+//                                            lane (c, grp), element u = token c, key 32s + 8grp + u
 //   QT   4096   [4 slabs][64 lanes][8 bf16]  Q~ = Q+ - M K+, same layout
-//   KD   8192   [4 pairs][64 lanes][8 bf16]  K^d, 16x16x16 A-operand layout of K^d^T tiles
+//   KD   8192   [4 pairs][64 lanes][8 bf16]  K^d, A-operand layout of K^d^T tiles: pair mp,
+//                                            lane (c, grp) = keys key_of(2mp, c), key_of(2mp + 1, c),
+//                                            tokens 4grp .. + 3
 //   TB   12288  [64 lanes][4 hi, 4 lo bf16]  T' = T diag(beta), 16x16x16 A-operand layout
 //   MM   13312  [64 lanes][4 hi, 4 lo bf16]  M = P T', same layout
-//   GAM  14336  [4 groups][32 fp32]          gamma = exp(G_C), permuted per lane group
+//   GAM  14336  [4 groups][32 fp32]          gamma = exp(G_C): group grp, entry 4m + i is the
+//                                            key of accumulator tile m, row 4grp + i
 constexpr int kRecW = 0;
 constexpr int kRecQT = 4096;
 constexpr int kRecKD = 8192;
@@ -45,9 +49,9 @@ constexpr int kBRecBytes = 12800;
 
 // A 128 x 128 state (or state gradient) of one (chunk, head) in bf16, as 32 MFMA
 // fragments of 1 KiB: fragment (ct, ks) at byte ((ct * 4 + ks) * 64 + lane) * 16 holds,
-// in lane (c, grp) = (lane % 16, lane / 16), value column 16 ct + c and key rows
-// 32 ks + 4 grp + i (elements i = 0..3) and 32 ks + 16 + 4 grp + i (elements 4..7):
-// the B operand of W S in the recurrent kernel, as that kernel holds it.
+// in lane (c, grp) = (lane % 16, lane / 16), value column 16 ct + c and keys
+// 32 ks + 8 grp + e (elements e = 0..7; rows 4grp + i of accumulator tiles 2ks and
+// 2ks + 1): the B operand of W S in the recurrent kernel, as that kernel holds it.
 constexpr int kStateBytesBf16 = 32768;
 
 // fp32 record for head dimension K: W, QT, KD [16][K]; TB, MM [16][16]; GAM [K] (all fp32).
