@@ -26,6 +26,7 @@
 #include "kda_device.h"
 #include "kda_gate_exact.h"
 #include "kda_internal.h"
+#include "kda_ring.h"
 
 namespace kda {
 namespace intra {
@@ -33,9 +34,9 @@ namespace intra {
 constexpr int KD = 128;
 constexpr int kChStride = 20;  // LDS elements per channel in channel-major tiles (16 tokens + 4 pad)
 
-// One wave's LDS. K^d, A and K+ have disjoint lifetimes and share one area:
-// K^d (A/P products -> its record store), A (forward substitution), K+ (W and
-// M K+ products). At 12.9 KiB per wave, three 4-wave workgroups fit in a CU.
+// One wave's LDS. The q and k tiles, K^d, A and K+ have disjoint lifetimes and share
+// one area: q and k (the loads, 8 KiB), K^d (A/P products -> its record store), A
+// (forward substitution), K+ (W and M K+ products). At 12.9 KiB per wave, three 4-wave workgroups fit in a CU.
 struct alignas(16) IntraLds {
     union {
         float kp[KD * kChStride];   // K+ channel-major [channel][token]
@@ -47,6 +48,7 @@ struct alignas(16) IntraLds {
     float gam[KD];  // gamma = exp(G_C) per channel
     float beta[16];
 };
+static_assert(sizeof(float) * KD * kChStride >= 2 * 16 * KD * sizeof(__bf16), "q and k tiles fit the K+ area");
 
 // Every wave works in its own LDS area, so ordering among the lanes of one wave is
 // all that is needed: LDS accesses of a wave execute in program order, and this
@@ -67,7 +69,7 @@ __device__ __forceinline__ void rec_store(char *p, const T &v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 
-// Eight consecutive bf16 values (one 16-byte load) as fp32.
+// Eight consecutive bf16 values (one 16-byte load, global or LDS) as fp32.
 __device__ __forceinline__ void load_bf16x8(const __bf16 *p, float *dst) {
     const uint4 raw = *reinterpret_cast<const uint4 *>(p);
     const unsigned int w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -95,17 +97,32 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
     const int grp = lane >> 4;
 
     // ---- load: lane holds token c, channels chan_of(e, grp) = 32s + 8grp + u (element
-    // e = 8s + u): one 16-byte load of q and of k per s ----
+    // e = 8s + u). q and k come by DMA (buffer_load ... lds) into the K+ area, free until
+    // the A / P products: whole 256-byte rows, four per wave-wide load, 16-byte chunk j of
+    // row r at slot j ^ r so that the per-lane reads below do not conflict; rows past the
+    // chunk read as zero. g is read directly, 16 bytes per load. ----
     const bool row_ok = c < len;
     const int64_t t = start + c;
     float kr[32], qr[32], gr[32];
     const size_t rowoff = ((size_t)(row_ok ? t : start) * H + h) * KD + 8 * grp;
     const float gs = (SCALAR_GATE && row_ok) ? g[(size_t)t * H + h] : 0.f;
+    char *tq = reinterpret_cast<char *>(L.kp), *tk = tq + 16 * KD * 2;
+    {
+        const unsigned int rowb = (unsigned int)H * KD * 2;  // one token row of q or k, bytes
+        const size_t row0 = ((size_t)start * H + h) * KD;
+        const int bytes = (int)((len - 1) * rowb + KD * 2);  // H <= 2^16: below 2^28
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q + row0, bytes), rk = rsrc(k + row0, bytes);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int r = 4 * s + (lane >> 4), j = (lane & 15) ^ r;
+            const unsigned int off = (unsigned int)r * rowb + 16u * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + 1024 * s), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + 1024 * s), 16, off, 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         if (row_ok) {
-            load_bf16x8(q + rowoff + 32 * s, qr + 8 * s);
-            load_bf16x8(k + rowoff + 32 * s, kr + 8 * s);
             if (SCALAR_GATE) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) gr[8 * s + u] = gs;
@@ -117,9 +134,18 @@ __device__ __forceinline__ void chunk_record(const __bf16 *__restrict__ q, const
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) { qr[8 * s + u] = 0.f; kr[8 * s + u] = 0.f; gr[8 * s + u] = 0.f; }
+            for (int u = 0; u < 8; ++u) gr[8 * s + u] = 0.f;
         }
     }
+    wait_vmcnt<0>();  // the DMA has landed (this wave's own loads)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int slot = c * KD * 2 + ((((4 * s + grp) ^ c) & 15) << 4);  // chunk 4s + grp of row c
+        load_bf16x8(reinterpret_cast<const __bf16 *>(tq + slot), qr + 8 * s);
+        load_bf16x8(reinterpret_cast<const __bf16 *>(tk + slot), kr + 8 * s);
+    }
+    wave_sync();  // read before the K^d writes below reuse the area
     const float b = row_ok ? beta[(size_t)t * H + h] : 0.f;
 
     // ---- running log-gate over the chunk's tokens (16-lane DPP scan), in place ----
