@@ -162,23 +162,53 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) I4[j] = (4 * grp + j == c) ? (short)0x3F80 : (short)0;
 
+    // q and k of the chunk as whole 256-byte rows by DMA into the K+ / K^d area, in the
+    // tile layout of tile_off<256> (16-byte chunk j of row r at slot j ^ r); rows past the
+    // chunk read as zero. Used for the chunk factors here and again before the key tiles.
+    char *tq = reinterpret_cast<char *>(L.kps);
+    char *tk = reinterpret_cast<char *>(L.kds);
+    auto dma_qk = [&]() {
+        // The offsets are recomputed at each call, not held in registers between the two
+        // calls: the opaque copy of the lane id keeps the compiler from sharing them, which
+        // would take the kernel past the register budget of two waves per SIMD.
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const unsigned int rowb = (unsigned int)H * KD * 2;  // one token row of q or k, bytes
+        const size_t row0 = ((size_t)start * H + h) * KD;
+        const int bytes = (int)((len - 1) * rowb + KD * 2);  // H <= 2^16: below 2^28
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q + row0, bytes), rk = rsrc(k + row0, bytes);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // rows 4s .. 4s + 3, 1 KiB per wave-wide load
+            const int r = 4 * s + (lane >> 4), j = (lane & 15) ^ r;  // LDS chunk lane & 15 holds chunk j
+            const unsigned int off = (unsigned int)r * rowb + 16u * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + 1024 * s), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + 1024 * s), 16, off, 0, 0, 0);
+        }
+    };
+
     // ================= 1. chunk factors (as the intra-chunk kernel) =================
     f32x4 pcol;  // P[4grp + i][c] (i <= r kept)
     bool exact;  // wave-uniform: this chunk takes the per-pair gate path (kda_gate_exact.h)
     {
         float kr[32], qr[32], G[32];
+        dma_qk();
+        float4 gl[8];  // g of token c, channels 32s + 8grp .. + 3 (gl[2s]) and + 4 .. + 7 (gl[2s + 1])
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {  // channels 32s + 8grp .. + 7: one 16-byte load of q and of k
-            uint4 qw = make_uint4(0u, 0u, 0u, 0u), kw = make_uint4(0u, 0u, 0u, 0u);
-            float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
-            if (row_ok) {
-                qw = *reinterpret_cast<const uint4 *>(q + krow + 32 * s + 8 * grp);
-                kw = *reinterpret_cast<const uint4 *>(k + krow + 32 * s + 8 * grp);
-                if (!SCALAR_GATE) {
-                    g0 = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp);
-                    g1 = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp + 4);
-                }
+        for (int s = 0; s < 4; ++s) {
+            gl[2 * s] = gl[2 * s + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row_ok && !SCALAR_GATE) {
+                gl[2 * s] = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp);
+                gl[2 * s + 1] = *reinterpret_cast<const float4 *>(g + krow + 32 * s + 8 * grp + 4);
             }
+        }
+        wait_vmcnt<0>();  // q and k have landed in LDS
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // channels 32s + 8grp .. + 7 of q and of k
+            const int cb = 2 * (32 * s + 8 * grp);
+            const uint4 qw = *reinterpret_cast<const uint4 *>(tq + tile_off<256>(c, cb));
+            const uint4 kw = *reinterpret_cast<const uint4 *>(tk + tile_off<256>(c, cb));
+            const float4 g0 = gl[2 * s], g1 = gl[2 * s + 1];
             const unsigned int qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -196,6 +226,7 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
             G[8 * s + 6] = g1.z;
             G[8 * s + 7] = g1.w;
         }
+        wave_sync();  // read before the K+ / K^d slabs below overwrite the area
         if (SCALAR_GATE) {
             const float gs = row_inclusive_sum(row_ok ? g[(size_t)tok * H + h] : 0.f);
 #pragma unroll
@@ -385,24 +416,10 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     wave_sync();
     // The key tiles need q, k and g again. q and k go straight to the K+ / K^d area,
     // free from here on, in the swizzled tile layout that later gathers dq and dk (each
-    // lane reads its inputs there before writing its outputs in the same place); rows
-    // past the chunk read as zero. g goes to registers, which the 16 x 16 backward
-    // leaves free. Both are in flight during that backward.
-    {
-        const unsigned int rowb = (unsigned int)H * KD * 2;  // one token row of q or k, bytes
-        const size_t row0 = ((size_t)start * H + h) * KD;
-        const int bytes = (int)((len - 1) * rowb + KD * 2);  // H <= 2^16: below 2^28
-        const __amdgpu_buffer_rsrc_t rq = rsrc(q + row0, bytes), rk = rsrc(k + row0, bytes);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {  // rows 4s .. 4s + 3, 1 KiB per wave-wide load
-            const int r = 4 * s + (lane >> 4), j = (lane & 15) ^ r;  // LDS chunk lane & 15 holds chunk j
-            const unsigned int off = (unsigned int)r * rowb + 16u * j;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(reinterpret_cast<char *>(L.kps) + 1024 * s),
-                                                     16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(reinterpret_cast<char *>(L.kds) + 1024 * s),
-                                                     16, off, 0, 0, 0);
-        }
-    }
+    // lane reads its inputs there before writing its outputs in the same place). g goes
+    // to registers, which the 16 x 16 backward leaves free. Both are in flight during
+    // that backward.
+    dma_qk();
     float4 gk[8];  // g of token c, channels key_of(kt, 4grp) .. + 3
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
@@ -482,8 +499,6 @@ __global__ __launch_bounds__(64 * kWaves) void kda_grad_bf16_kernel(
     wait_vmcnt<0>();  // q and k have landed in LDS
     wave_sync();  // the matrices' area now gathers dg, the K+/K^d area dq and dk
     char *tg = reinterpret_cast<char *>(L.a);
-    char *tq = reinterpret_cast<char *>(L.kps);
-    char *tk = reinterpret_cast<char *>(L.kds);
     // One key tile; EXACT: the chunk's decay is too strong for the factored gate form,
     // so the products of A~ and P with the gates are differentiated pair by pair.
     auto key_tile = [&](int kt, auto exact_tag) {
