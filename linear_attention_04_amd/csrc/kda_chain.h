@@ -62,6 +62,7 @@ struct LaneOffsets {
     unsigned int v2;     // NW = 4: the second value tile load (token rows 8 .. 15)
     unsigned int out;    // output: token c, columns col + 4grp .. + 3, within the chunk
     unsigned int vrow;   // one token row of v / out in bytes (H * VD * 2)
+    unsigned int stage;  // staged output (4-tile whole-tile form): byte in a staging buffer
 };
 
 
@@ -119,6 +120,20 @@ constexpr int kXchgSlots = 3;
 template <int NW>
 constexpr int xchg_bytes() { return 2 * NW * kXchgSlots * 1024; }
 constexpr int kXchgBytes = xchg_bytes<kNW>();
+
+// Output staging of the 4-tile whole-tile form. Its compute waves write each chunk's
+// output tile (16 token rows x 64 columns, bf16) to LDS, and a store wave writes it to
+// HBM as whole 128-byte rows, so the compute waves issue no global stores. Two chunk
+// buffers; rows padded to 144 bytes so that the compute waves' 8-byte writes spread
+// over the banks. Every wave of the workgroup passes one extra barrier at the end, after
+// which the store wave takes the last chunk's output.
+constexpr int kStageRow = 144;
+constexpr int kStageBytes = 16 * kStageRow;
+constexpr int kStageBufs = 2;
+template <int NW, bool FULL>
+constexpr bool staged_out() { return FULL && NW == 4; }
+template <int NW, bool FULL>
+constexpr int stage_bytes() { return staged_out<NW, FULL>() ? kStageBufs * kStageBytes : 0; }
 
 // One chunk's operands for one half, in registers (read from the ring slot ahead of use).
 struct HalfOps {
@@ -430,9 +445,11 @@ __device__ __forceinline__ void tile_part_a(const TileOps &o, f32x4 (&S)[8], f32
 
 // After the barrier: Delta = T' V - W S, the state update of all eight tiles and
 // the output store.
-template <bool OUT, int NW>
+// ST: the output goes to the LDS staging buffer `stage`, not to `ochunk`.
+template <bool OUT, int NW, bool ST = false>
 __device__ __forceinline__ void tile_part_b(const TileOps &o, f32x4 (&S)[8], const f32x4 &x0, const f32x4 &x1,
-                                            const f32x4 &y, char *ochunk, int len, const LaneOffsets &lo) {
+                                            const f32x4 &y, char *ochunk, int len, const LaneOffsets &lo,
+                                            char *stage = nullptr) {
     const f32x4 d = -(x0 + x1);
     unsigned int h01, h23, l01, l23;
     split_pair(d[0], d[1], h01, l01);
@@ -441,16 +458,26 @@ __device__ __forceinline__ void tile_part_b(const TileOps &o, f32x4 (&S)[8], con
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = mfma_16x16x32(o.kd[m], db, S[m]);
     if (OUT) {
-        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+        if (ST) {
+            *reinterpret_cast<u32x2 *>(stage + lo.stage) = packed;
+            // Issued here, a chunk step before the wait on it: left to the scheduler, the
+            // write sinks to just before that wait and its latency lands on the chain.
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
+            __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+        }
     }
 }
 
 // The chunk loop of the whole-tile compute wave of tile vt; barriers as in
 // compute_wave (B_j publishes chunk j's ring slot).
-template <int DEPTH, bool OUT, int NW, class Sync>
+// STAGE: chunk j's output goes to staging buffer j % 2 after the ring, for the store
+// wave (store_wave). A compute wave writes it after B_{j+1} and waits for its LDS
+// accesses before B_{j+2}; after the last chunk it passes the extra barrier B_{nchunks+1}.
+template <int DEPTH, bool OUT, int NW, bool STAGE, class Sync>
 __device__ __forceinline__ void compute_wave_full(f32x4 (&S)[8], char *ring, int64_t nchunks, int64_t tok_rows,
                                                   char *o0, size_t chunk_rows, int vt, int lane,
                                                   const LaneOffsets &lo, Sync &sync) {
@@ -461,27 +488,35 @@ __device__ __forceinline__ void compute_wave_full(f32x4 (&S)[8], char *ring, int
         const int64_t rem = tok_rows - 16 * j;
         return rem <= 0 ? 0 : (rem >= 16 ? 16 : (int)rem);
     };
-    auto step = [&](int64_t j, const TileOps &cur, TileOps &next) {
+    char *const stage0 = ring + DEPTH * slot_bytes<NW>();
+    // buf: chunk j's staging buffer, j % 2 (the loop's steps start at even j)
+    auto step = [&](int64_t j, const TileOps &cur, TileOps &next, int buf) {
         f32x4 x0, x1, y;
         tile_part_a<OUT>(cur, S, x0, x1, y);
-        sync.barrier(j + 1);  // B_{j+1}
+        if (STAGE) wait_lgkm0();  // the previous chunk's staged output is in LDS
+        sync.barrier(j + 1);      // B_{j+1}
         read_tile_ops<NW>(next, slot_of(j + 1), vt, lane);
-        tile_part_b<OUT, NW>(cur, S, x0, x1, y, OUT ? o0 + (size_t)j * chunk_rows : nullptr, len_of(j), lo);
+        tile_part_b<OUT, NW, STAGE>(cur, S, x0, x1, y, OUT ? o0 + (size_t)j * chunk_rows : nullptr, len_of(j), lo,
+                                    stage0 + buf * kStageBytes);
     };
     TileOps opa, opb;
     sync.barrier(0);  // B_0
     read_tile_ops<NW>(opa, slot_of(0), vt, lane);
     int64_t j = 0;
     for (; j + 2 <= nchunks; j += 2) {
-        step(j, opa, opb);
-        step(j + 1, opb, opa);
+        step(j, opa, opb, 0);
+        step(j + 1, opb, opa, 1);
     }
-    if (j < nchunks) step(j, opa, opb);
+    if (j < nchunks) step(j, opa, opb, 0);
+    if (STAGE) {
+        wait_lgkm0();
+        sync.barrier(nchunks + 1);  // B_{nchunks+1}: the last chunk's staged output is in LDS
+    }
 }
 
 // compute_role for the whole-tile form: compute wave vt owns value columns
 // col0 + 16 vt .. + 15 and all 128 key rows.
-template <int DEPTH, bool OUT, int NW, class Sync>
+template <int DEPTH, bool OUT, int NW, bool STAGE, class Sync>
 __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, int pair, int col0,
                                                   const SeqChunks &sc, size_t tok_bytes, size_t chunk_rows,
                                                   LaneOffsets lo, const float *__restrict__ s0,
@@ -489,6 +524,7 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
                                                   Sync &sync) {
     const int c = lane & 15, grp = lane >> 4;
     lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;
+    lo.stage = c * kStageRow + (vt * 16 + 4 * grp) * 2;
     f32x4 S[8];
     const size_t sbase = (size_t)pair * KD * VD + col0 + vt * 16 + c;
     if (s0) {
@@ -502,8 +538,8 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
     }
     wait_vmcnt<0>();  // as in compute_role: no state load left for the loop's counter waits
     char *o0 = OUT ? reinterpret_cast<char *>(out) + tok_bytes : nullptr;
-    compute_wave_full<DEPTH, OUT, NW>(S, ring, sc.chunk_end - sc.chunk_begin, sc.tok_end - sc.tok_begin, o0,
-                                      chunk_rows, vt, lane, lo, sync);
+    compute_wave_full<DEPTH, OUT, NW, STAGE>(S, ring, sc.chunk_end - sc.chunk_begin, sc.tok_end - sc.tok_begin,
+                                             o0, chunk_rows, vt, lane, lo, sync);
     if (sT) {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -512,6 +548,35 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
     }
 }
 
+
+// The store wave of the staged form: chunk j's output tile leaves staging buffer j % 2
+// after barrier B_{j+2}, by which the compute waves have written it (after B_{j+1},
+// waiting for the writes before B_{j+2}), and before B_{j+3}, after which they write
+// the buffer again. Rows past a short last chunk are dropped by the buffer range. It
+// passes the same nchunks + 2 barriers as the other waves. Lane l stores bytes
+// 16 (l % 8) .. + 15 of rows l / 8 and l / 8 + 8.
+template <int DEPTH, int NW, class Sync>
+__device__ __forceinline__ void store_wave(char *ring, int64_t nchunks, int64_t tok_rows, char *o0,
+                                           size_t chunk_rows, int lane, unsigned int vrow, Sync &sync) {
+    static_assert(NW == 4, "a staged row is 128 bytes");
+    const char *stage0 = ring + DEPTH * slot_bytes<NW>();
+    const int r = lane >> 3, p = lane & 7;
+    const unsigned int off = (unsigned int)r * vrow + 16u * p;
+    sync.barrier(0);  // B_0
+    sync.barrier(1);  // B_1
+    for (int64_t j = 0; j < nchunks; ++j) {
+        sync.barrier(j + 2);  // B_{j+2}
+        const int64_t rem = tok_rows - 16 * j;
+        const int len = rem >= 16 ? 16 : (int)rem;  // >= 1
+        const char *st = stage0 + (int)(j & 1) * kStageBytes;
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(st + r * kStageRow + 16 * p);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(st + (r + 8) * kStageRow + 16 * p);
+        const __amdgpu_buffer_rsrc_t ro = rsrc(o0 + (size_t)j * chunk_rows, tile_bytes<NW>(len, vrow));
+        __builtin_amdgcn_raw_buffer_store_b128(a, ro, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(b, ro, off + 8 * vrow, 0, 0);
+    }
+}
 
 // The hardware workgroup barrier: every wave of the workgroup takes part.
 struct HwSync {

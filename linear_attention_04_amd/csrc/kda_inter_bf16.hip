@@ -47,7 +47,7 @@ namespace {
 template <int NW, bool FULL>
 constexpr int inter_compute_waves() { return FULL ? NW : compute_waves<NW>(); }
 template <int NW, bool FULL>
-constexpr int inter_waves() { return inter_compute_waves<NW, FULL>() + kProducers; }
+constexpr int inter_waves() { return inter_compute_waves<NW, FULL>() + kProducers + (staged_out<NW, FULL>() ? 1 : 0); }
 template <int NW, bool FULL>
 constexpr int inter_xchg_bytes() { return FULL ? 0 : xchg_bytes<NW>(); }
 
@@ -82,6 +82,15 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
 
+    if constexpr (staged_out<NW, FULL>()) {
+        if (wid == inter_waves<NW, FULL>() - 1) {
+            // ---- output store wave ----
+            HwSync ssync;
+            store_wave<DEPTH, NW>(ring, nchunks, sc.tok_end - sc.tok_begin, reinterpret_cast<char *>(out) + tok_bytes,
+                                  chunk_rows, lane, lo.vrow, ssync);
+            return;
+        }
+    }
     if (wid >= inter_compute_waves<NW, FULL>()) {
         // ---- producer ----
         const int p = wid - inter_compute_waves<NW, FULL>();
@@ -117,13 +126,14 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
             if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
         }
         barrier();  // B_nchunks
+        if (staged_out<NW, FULL>()) barrier();  // B_{nchunks+1}, for the output store wave
         return;
     }
 
     HwSync sync;
     if (FULL) {
-        compute_role_full<DEPTH, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
-                                          OUT ? sT : nullptr, sync);
+        compute_role_full<DEPTH, OUT, NW, staged_out<NW, FULL>()>(ring, wid, lane, pair, col0, sc, tok_bytes,
+                                                                  chunk_rows, lo, s0, out, OUT ? sT : nullptr, sync);
         return;
     }
     // chunk start states, chunk-major like the records: chunk j of this pair is H states on
@@ -140,7 +150,7 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>();
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>() + stage_bytes<NW, FULL>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW, FULL>;
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);

@@ -340,9 +340,17 @@ def test_bf16_head_counts_not_multiple_of_four(H):
 
 def test_bf16_four_tile_workgroups():
     """120 (sequence, head) pairs: too many for one 2-tile recurrent workgroup per CU,
-    so 4-tile ones (8 compute waves sharing one record stream), with ragged and empty
-    packed sequences."""
+    so 4-tile ones (four compute waves sharing one record stream, and a wave that
+    stores their outputs from LDS), with ragged and empty packed sequences."""
     w, x = _case("bf16_nw4", 124, H=24, state=True, lengths=[1, 15, 0, 33, 100])
+    _check(w, x, True)
+
+
+def test_bf16_four_tile_staged_output_chunk_counts():
+    """The 4-tile form's outputs leave through LDS staging buffers (two, used in turn)
+    and a store wave that takes the last chunk's after one extra barrier: sequences of
+    one, two, three and four chunks, full and short last chunks, at 144 pairs."""
+    w, x = _case("bf16_nw4_stage", 125, H=24, state=True, lengths=[16, 17, 32, 2, 48, 31])
     _check(w, x, True)
 
 
