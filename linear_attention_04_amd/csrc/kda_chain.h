@@ -386,14 +386,27 @@ __device__ __forceinline__ void read_tile_ops(TileOps &o, const char *slot, int 
         o.w[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecW + (s * 64 + lane) * 16);
         o.qt[s] = *reinterpret_cast<const bf16x8 *>(slot + kRecQT + (s * 64 + lane) * 16);
     }
+    // [K^d; K^d]: with two tiles per workgroup, two reads of the same 8 bytes (the
+    // volatile keeps them apart), which costs the chain less than two register copies;
+    // with four, whose compute waves share the CU's LDS bandwidth, one read copied.
     typedef const volatile __attribute__((address_space(3))) unsigned long long lds_u64;
+    if (NW == 4) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        lds_u64 *pk = (lds_u64 *)(slot + kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8);
-        const unsigned long long a = *pk;
-        const unsigned long long b = *pk;
-        o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b,
-                                                        (unsigned)(b >> 32)));
+        for (int m = 0; m < 8; ++m) {
+            const unsigned long long a = *reinterpret_cast<const unsigned long long *>(
+                slot + kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8);
+            o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)a,
+                                                            (unsigned)(a >> 32)));
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            lds_u64 *pk = (lds_u64 *)(slot + kRecKD + ((m >> 1) * 64 + lane) * 16 + (m & 1) * 8);
+            const unsigned long long a = *pk;
+            const unsigned long long b = *pk;
+            o.kd[m] = __builtin_bit_cast(bf16x8, make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b,
+                                                            (unsigned)(b >> 32)));
+        }
     }
     o.tb = *reinterpret_cast<const bf16x8 *>(slot + kRecTB + lane * 16);
     o.mm = *reinterpret_cast<const bf16x8 *>(slot + kRecMM + lane * 16);
