@@ -135,6 +135,19 @@ constexpr bool staged_out() { return FULL && NW == 4; }
 template <int NW, bool FULL>
 constexpr int stage_bytes() { return staged_out<NW, FULL>() ? kStageBufs * kStageBytes : 0; }
 
+// Saved-state staging of the training forward (the 2-tile two-wave form with SAVE and
+// OUT). Its compute waves write each chunk's start state, the workgroup's eight 1 KiB
+// bf16 fragments, to LDS, and a store wave writes them to HBM after the chunk's
+// barrier, so the chain's waves issue none of the 1 GiB of state stores (at H=64,
+// T=8192) themselves. Two chunk buffers after the exchange area. The backward's
+// recomputed forward (SAVE without OUT) stores its states directly: staged, it was
+// slower.
+constexpr int kSaveStageBytes = 2 * 4096;
+template <int NW, bool SAVE, bool OUT>
+constexpr bool staged_save() { return SAVE && OUT && NW == 2; }
+template <int NW, bool SAVE, bool OUT>
+constexpr int save_stage_bytes() { return staged_save<NW, SAVE, OUT>() ? 2 * kSaveStageBytes : 0; }
+
 // One chunk's operands for one half, in registers (read from the ring slot ahead of use).
 struct HalfOps {
     bf16x8 w[2], qt[2];  // slabs 2 kh, 2 kh + 1 of W and Q~
@@ -179,9 +192,10 @@ __device__ __forceinline__ void read_ops(HalfOps &o, const char *slot, int vt, i
 // First half of a chunk step, before the barrier: partial W S and Q~ S over this
 // wave's rows, published to the partner; then the decay of this wave's rows.
 // SAVE (the forward for a backward pass): the chunk's start state goes to `sdst` as
-// bf16 fragments (ct, 2 KH) and (ct, 2 KH + 1). OUT: the output's partial products
-// are formed (a recomputed forward that only saves states skips them).
-template <int KH, bool SAVE = false, bool OUT = true>
+// bf16 fragments (ct, 2 KH) and (ct, 2 KH + 1), in HBM, or with SST in the LDS staging
+// buffer. OUT: the output's partial products are formed (a recomputed forward that
+// only saves states skips them).
+template <int KH, bool SAVE = false, bool OUT = true, bool SST = false>
 __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f32x4 &x, f32x4 &y,
                                              char *xchg, int lane, char *sdst = nullptr) {
     bf16x8 sb[2];
@@ -200,8 +214,13 @@ __device__ __forceinline__ void chunk_part_a(const HalfOps &o, f32x4 (&S)[4], f3
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if (SAVE) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), reinterpret_cast<u32x4 *>(sdst));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), reinterpret_cast<u32x4 *>(sdst + 1024));
+        if (SST) {
+            *reinterpret_cast<u32x4 *>(sdst) = __builtin_bit_cast(u32x4, sb[0]);
+            *reinterpret_cast<u32x4 *>(sdst + 1024) = __builtin_bit_cast(u32x4, sb[1]);
+        } else {
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), reinterpret_cast<u32x4 *>(sdst));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), reinterpret_cast<u32x4 *>(sdst + 1024));
+        }
     }
     x = mfma_16x16x32(o.w[0], sb[0], zero);
     if (OUT) y = mfma_16x16x32(sb[0], o.qt[0], zero);
@@ -263,8 +282,10 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
 
 // The chunk loop of compute wave (vt, KH). Barrier B_j (j = 0 .. nchunks) is passed
 // once by every wave of the workgroup: B_j (j < nchunks) publishes chunk j's ring
-// slot, and B_{j+1} also publishes the partial products of chunk j.
-template <int KH, int DEPTH, bool SAVE, bool OUT, int NW, class Sync>
+// slot, and B_{j+1} also publishes the partial products of chunk j (and with SST, the
+// chunk's start state in staging buffer j % 2, `sdst0` being this wave's place in
+// buffer 0).
+template <int KH, int DEPTH, bool SAVE, bool OUT, int NW, bool SST, class Sync>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
                                              char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
                                              Sync &sync, char *sdst0 = nullptr, size_t sstride = 0) {
@@ -284,8 +305,10 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
         f32x4 x, y, px, py;
         char *xc = xchg_of(j);
-        chunk_part_a<KH, SAVE, OUT>(cur, S, x, y, xc, lane, SAVE ? sdst0 + (size_t)j * sstride : nullptr);
-        wait_lgkm0();  // the partial products are in LDS before the barrier
+        char *sdst = !SAVE ? nullptr : SST ? sdst0 + (int)(j & 1) * kSaveStageBytes : sdst0 + (size_t)j * sstride;
+        chunk_part_a<KH, SAVE, OUT, SST>(cur, S, x, y, xc, lane, sdst);
+        if (SST) asm volatile("" ::: "memory");  // the staged state is written before the wait
+        wait_lgkm0();  // the partial products (and a staged state) are in LDS before the barrier
         sync.barrier(j + 1);  // B_{j+1}
         read_partner<KH, OUT>(xc, lane, px, py);
         read_ops<KH, NW>(next, slot_of(j + 1), vt, lane);
@@ -309,7 +332,7 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 // the sequence's first chunk in the [max_chunks][H] array of chunk start states, and
 // `sstride` is the distance between a pair's consecutive chunks there.
 // OUT: the chunk outputs go to `out`. The final state goes to `sT` unless it is NULL.
-template <int DEPTH, bool SAVE, bool OUT, int NW, class Sync>
+template <int DEPTH, bool SAVE, bool OUT, int NW, bool SST, class Sync>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
@@ -336,14 +359,17 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     char *o0 = OUT ? reinterpret_cast<char *>(out) + tok_bytes : nullptr;
     const int64_t nchunks = sc.chunk_end - sc.chunk_begin;
     const int64_t tok_rows = sc.tok_end - sc.tok_begin;
-    // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile
-    char *sdst0 = SAVE ? states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16 : nullptr;
+    // fragment (ct, 2 kh) of each chunk start state, ct = this wave's value tile; with
+    // SST its place in the staging buffer, which holds the workgroup's fragments in order
+    char *sdst0 = !SAVE ? nullptr
+                  : SST ? ring + DEPTH * slot_bytes<NW>() + xchg_bytes<NW>() + ((vt * 4 + 2 * kh) * 64 + lane) * 16
+                        : states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16;
     if (kh == 0)
-        compute_wave<0, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0,
-                                              sstride);
+        compute_wave<0, DEPTH, SAVE, OUT, NW, SST>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync,
+                                                   sdst0, sstride);
     else
-        compute_wave<1, DEPTH, SAVE, OUT, NW>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync, sdst0,
-                                              sstride);
+        compute_wave<1, DEPTH, SAVE, OUT, NW, SST>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync,
+                                                   sdst0, sstride);
 
     if (sT) {
 #pragma unroll
@@ -588,6 +614,31 @@ __device__ __forceinline__ void store_wave(char *ring, int64_t nchunks, int64_t 
         const __amdgpu_buffer_rsrc_t ro = rsrc(o0 + (size_t)j * chunk_rows, tile_bytes<NW>(len, vrow));
         __builtin_amdgcn_raw_buffer_store_b128(a, ro, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(b, ro, off + 8 * vrow, 0, 0);
+    }
+}
+
+// The store wave of the staged two-wave form with SAVE: chunk j's start state (the
+// workgroup's 8 KiB of fragments, in HBM order) leaves staging buffer j % 2 after
+// B_{j+1}, by which the compute waves have written it, and before B_{j+2}, after which
+// they write the buffer again. `block0`: the workgroup's first fragment of the
+// sequence's first chunk; chunk j's is `sstride` bytes further per chunk. It passes
+// the same nchunks + 1 barriers as the other waves.
+template <int DEPTH, int NW, class Sync>
+__device__ __forceinline__ void save_store_wave(char *ring, int64_t nchunks, char *block0, size_t sstride,
+                                                int lane, Sync &sync) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kFrags = kSaveStageBytes / 1024;
+    const char *stage0 = ring + DEPTH * slot_bytes<NW>() + xchg_bytes<NW>() + lane * 16;
+    sync.barrier(0);  // B_0
+    for (int64_t j = 0; j < nchunks; ++j) {
+        sync.barrier(j + 1);  // B_{j+1}
+        const char *st = stage0 + (int)(j & 1) * kSaveStageBytes;
+        char *dst = block0 + (size_t)j * sstride + lane * 16;
+        u32x4 f[kFrags];
+#pragma unroll
+        for (int k = 0; k < kFrags; ++k) f[k] = *reinterpret_cast<const u32x4 *>(st + k * 1024);
+#pragma unroll
+        for (int k = 0; k < kFrags; ++k) __builtin_nontemporal_store(f[k], reinterpret_cast<u32x4 *>(dst + k * 1024));
     }
 }
 

@@ -46,13 +46,17 @@ namespace {
 // wave per tile (compute_role_full) instead of two (compute_role); the prefill's form.
 template <int NW, bool FULL>
 constexpr int inter_compute_waves() { return FULL ? NW : compute_waves<NW>(); }
-template <int NW, bool FULL>
-constexpr int inter_waves() { return inter_compute_waves<NW, FULL>() + kProducers + (staged_out<NW, FULL>() ? 1 : 0); }
+// a store wave when outputs (staged_out) or saved states (staged_save) go through LDS
+template <int NW, bool FULL, bool SAVE, bool OUT>
+constexpr int inter_waves() {
+    return inter_compute_waves<NW, FULL>() + kProducers +
+           ((staged_out<NW, FULL>() || staged_save<NW, SAVE, OUT>()) ? 1 : 0);
+}
 template <int NW, bool FULL>
 constexpr int inter_xchg_bytes() { return FULL ? 0 : xchg_bytes<NW>(); }
 
 template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>
-__global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16_kernel(
+__global__ __launch_bounds__((64 * inter_waves<NW, FULL, SAVE, OUT>())) void kda_inter_bf16_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const float *__restrict__ s0, unsigned short *__restrict__ out,
     float *__restrict__ sT, int64_t T, int H, int N, int64_t max_chunks,
@@ -82,8 +86,17 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
     const size_t tok_bytes = ((size_t)sc.tok_begin * H + h) * VD * 2 + (size_t)col0 * 2;
     const size_t chunk_rows = (size_t)16 * lo.vrow;  // bytes of 16 token rows
 
+    if constexpr (staged_save<NW, SAVE, OUT>()) {
+        if (wid == inter_waves<NW, FULL, SAVE, OUT>() - 1) {
+            // ---- saved-state store wave ----
+            HwSync ssync;
+            char *block0 = states + ((size_t)sc.chunk_begin * H + h) * kStateBytesBf16 + (size_t)(col0 >> 4) * 4096;
+            save_store_wave<DEPTH, NW>(ring, nchunks, block0, (size_t)H * kStateBytesBf16, lane, ssync);
+            return;
+        }
+    }
     if constexpr (staged_out<NW, FULL>()) {
-        if (wid == inter_waves<NW, FULL>() - 1) {
+        if (wid == inter_waves<NW, FULL, SAVE, OUT>() - 1) {
             // ---- output store wave ----
             HwSync ssync;
             store_wave<DEPTH, NW>(ring, nchunks, sc.tok_end - sc.tok_begin, reinterpret_cast<char *>(out) + tok_bytes,
@@ -139,8 +152,9 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL>())) void kda_inter_bf16
     // chunk start states, chunk-major like the records: chunk j of this pair is H states on
     char *st = SAVE ? states + ((size_t)sc.chunk_begin * H + h) * kStateBytesBf16 : nullptr;
     const size_t sstride = (size_t)H * kStateBytesBf16;
-    compute_role<DEPTH, SAVE, OUT, NW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out,
-                                       OUT ? sT : nullptr, sync, st, sstride);
+    compute_role<DEPTH, SAVE, OUT, NW, staged_save<NW, SAVE, OUT>()>(ring, wid, lane, pair, col0, sc, tok_bytes,
+                                                                       chunk_rows, lo, s0, out, OUT ? sT : nullptr,
+                                                                       sync, st, sstride);
 }
 
 template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>
@@ -150,12 +164,13 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>() + stage_bytes<NW, FULL>();
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>() + stage_bytes<NW, FULL>() +
+                           save_stage_bytes<NW, SAVE, OUT>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW, FULL>;
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * inter_waves<NW, FULL>()), lds, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * inter_waves<NW, FULL, SAVE, OUT>()), lds, stream,
                        static_cast<const unsigned short *>(v), cu_seqlens, chunk_off, s0,
                        static_cast<unsigned short *>(out), sT, geo.T, geo.H, geo.N, geo.max_chunks,
                        base + geo.off_records, SAVE ? const_cast<char *>(base) + geo.off_states : nullptr,
@@ -238,7 +253,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
         return;
     }
     HwSync sync;
-    compute_role<kFusedDepth, false, true, kNW>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT,
+    compute_role<kFusedDepth, false, true, kNW, false>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT,
                                                 sync);
 }
 
