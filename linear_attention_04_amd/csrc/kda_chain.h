@@ -121,19 +121,20 @@ template <int NW>
 constexpr int xchg_bytes() { return 2 * NW * kXchgSlots * 1024; }
 constexpr int kXchgBytes = xchg_bytes<kNW>();
 
-// Output staging of the 4-tile whole-tile form. Its compute waves write each chunk's
-// output tile (16 token rows x 64 columns, bf16) to LDS, and a store wave writes it to
-// HBM as whole 128-byte rows, so the compute waves issue no global stores. Two chunk
-// buffers; rows padded to 144 bytes so that the compute waves' 8-byte writes spread
-// over the banks. Every wave of the workgroup passes one extra barrier at the end, after
-// which the store wave takes the last chunk's output.
+// Output staging of the 4-tile forms (both the one-wave and the two-wave form). The
+// compute waves that form the output write each chunk's output tile (16 token rows x 64
+// columns, bf16) to LDS, and a store wave writes it to HBM as whole 128-byte rows, so
+// the compute waves issue no global stores. Two chunk buffers after the ring (and the
+// exchange area of the two-wave form); rows padded to 144 bytes so that the compute
+// waves' 8-byte writes spread over the banks. Every wave of the workgroup passes one
+// extra barrier at the end, after which the store wave takes the last chunk's output.
 constexpr int kStageRow = 144;
 constexpr int kStageBytes = 16 * kStageRow;
 constexpr int kStageBufs = 2;
-template <int NW, bool FULL>
-constexpr bool staged_out() { return FULL && NW == 4; }
-template <int NW, bool FULL>
-constexpr int stage_bytes() { return staged_out<NW, FULL>() ? kStageBufs * kStageBytes : 0; }
+template <int NW, bool OUT>
+constexpr bool staged_out() { return OUT && NW == 4; }
+template <int NW, bool OUT>
+constexpr int stage_bytes() { return staged_out<NW, OUT>() ? kStageBufs * kStageBytes : 0; }
 
 // Saved-state staging of the training forward (the 2-tile two-wave form with SAVE and
 // OUT). Its compute waves write each chunk's start state, the workgroup's eight 1 KiB
@@ -255,10 +256,11 @@ __device__ __forceinline__ void read_partner(const char *xchg, int lane, f32x4 &
 // Second half, after the barrier: Delta = T' V - W S from both parts (the two
 // halves form the same sum, so they hold bitwise equal Delta), the state update of
 // this wave's rows and, on half 0, the output.
-template <int KH, bool OUT, int NW>
+// STO: the output goes to the LDS staging buffer `stage`, not to `ochunk`.
+template <int KH, bool OUT, int NW, bool STO = false>
 __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], const f32x4 &x, const f32x4 &y,
                                              const f32x4 &px, const f32x4 &py, char *ochunk, int len,
-                                             const LaneOffsets &lo) {
+                                             const LaneOffsets &lo, char *stage = nullptr) {
     const f32x4 x0 = KH == 0 ? x : px;
     const f32x4 z1 = KH == 0 ? px : x;
     const f32x4 d = -(x0 + z1);
@@ -272,10 +274,15 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
         const f32x4 yt = y + py;
         // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
         // end of a short chunk fall outside the descriptor and are dropped
-        const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 packed = {pack_bf16x2(yt[0], yt[1]), pack_bf16x2(yt[2], yt[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+        if (STO) {
+            *reinterpret_cast<u32x2 *>(stage + lo.stage) = packed;
+            __builtin_amdgcn_sched_barrier(0);  // as in tile_part_b
+        } else {
+            const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
+            __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
+        }
     }
 }
 
@@ -285,7 +292,7 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
 // slot, and B_{j+1} also publishes the partial products of chunk j (and with SST, the
 // chunk's start state in staging buffer j % 2, `sdst0` being this wave's place in
 // buffer 0).
-template <int KH, int DEPTH, bool SAVE, bool OUT, int NW, bool SST, class Sync>
+template <int KH, int DEPTH, bool SAVE, bool OUT, int NW, bool SST, bool STO, class Sync>
 __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t nchunks, int64_t tok_rows,
                                              char *o0, size_t chunk_rows, int vt, int lane, const LaneOffsets &lo,
                                              Sync &sync, char *sdst0 = nullptr, size_t sstride = 0) {
@@ -302,7 +309,10 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
     // Every step reads the next slot, also after the last chunk: that read lands in
     // LDS the workgroup owns and its values are never used, and it keeps the loop
     // body free of branches.
-    auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next) {
+    // STO: chunk j's output goes to staging buffer `buf` = j % 2 (the loop's steps start
+    // at even j), waited for before B_{j+2} like the partial products
+    char *const ostage0 = ring + DEPTH * slot_bytes<NW>() + xchg_bytes<NW>();
+    auto step = [&](int64_t j, const HalfOps &cur, HalfOps &next, int buf) {
         f32x4 x, y, px, py;
         char *xc = xchg_of(j);
         char *sdst = !SAVE ? nullptr : SST ? sdst0 + (int)(j & 1) * kSaveStageBytes : sdst0 + (size_t)j * sstride;
@@ -312,18 +322,22 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
         sync.barrier(j + 1);  // B_{j+1}
         read_partner<KH, OUT>(xc, lane, px, py);
         read_ops<KH, NW>(next, slot_of(j + 1), vt, lane);
-        chunk_part_b<KH, OUT, NW>(cur, S, x, y, px, py, OUT ? o0 + (size_t)j * chunk_rows : nullptr, len_of(j),
-                                   lo);
+        chunk_part_b<KH, OUT, NW, STO>(cur, S, x, y, px, py, OUT ? o0 + (size_t)j * chunk_rows : nullptr,
+                                        len_of(j), lo, ostage0 + buf * kStageBytes);
     };
     HalfOps opa, opb;
     sync.barrier(0);  // B_0
     read_ops<KH, NW>(opa, slot_of(0), vt, lane);
     int64_t j = 0;
     for (; j + 2 <= nchunks; j += 2) {
-        step(j, opa, opb);
-        step(j + 1, opb, opa);
+        step(j, opa, opb, 0);
+        step(j + 1, opb, opa, 1);
     }
-    if (j < nchunks) step(j, opa, opb);
+    if (j < nchunks) step(j, opa, opb, 0);
+    if (STO) {
+        wait_lgkm0();
+        sync.barrier(nchunks + 1);  // B_{nchunks+1}: the last chunk's staged output is in LDS
+    }
 }
 
 // The compute waves' part of a recurrent workgroup: the state slice in, the chunk
@@ -332,7 +346,7 @@ __device__ __forceinline__ void compute_wave(f32x4 (&S)[4], char *ring, int64_t 
 // the sequence's first chunk in the [max_chunks][H] array of chunk start states, and
 // `sstride` is the distance between a pair's consecutive chunks there.
 // OUT: the chunk outputs go to `out`. The final state goes to `sT` unless it is NULL.
-template <int DEPTH, bool SAVE, bool OUT, int NW, bool SST, class Sync>
+template <int DEPTH, bool SAVE, bool OUT, int NW, bool SST, bool STO, class Sync>
 __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int pair, int col0, const SeqChunks &sc,
                                              size_t tok_bytes, size_t chunk_rows, LaneOffsets lo,
                                              const float *__restrict__ s0, unsigned short *__restrict__ out,
@@ -341,6 +355,7 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
     const int c = lane & 15, grp = lane >> 4;
     const int vt = wid >> 1, kh = wid & 1;
     lo.out = c * lo.vrow + (vt * 16 + 4 * grp) * 2;  // token c, columns 4grp .. + 3 of the tile
+    lo.stage = c * kStageRow + (vt * 16 + 4 * grp) * 2;
     f32x4 S[4];
     const size_t sbase = (size_t)pair * KD * VD + (size_t)(64 * kh) * VD + col0 + vt * 16 + c;
     if (s0) {
@@ -365,11 +380,11 @@ __device__ __forceinline__ void compute_role(char *ring, int wid, int lane, int 
                   : SST ? ring + DEPTH * slot_bytes<NW>() + xchg_bytes<NW>() + ((vt * 4 + 2 * kh) * 64 + lane) * 16
                         : states + ((size_t)(((col0 >> 4) + vt) * 4 + 2 * kh) * 64 + lane) * 16;
     if (kh == 0)
-        compute_wave<0, DEPTH, SAVE, OUT, NW, SST>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync,
-                                                   sdst0, sstride);
+        compute_wave<0, DEPTH, SAVE, OUT, NW, SST, STO>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo,
+                                                        sync, sdst0, sstride);
     else
-        compute_wave<1, DEPTH, SAVE, OUT, NW, SST>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo, sync,
-                                                   sdst0, sstride);
+        compute_wave<1, DEPTH, SAVE, OUT, NW, SST, STO>(S, ring, nchunks, tok_rows, o0, chunk_rows, vt, lane, lo,
+                                                        sync, sdst0, sstride);
 
     if (sT) {
 #pragma unroll
@@ -594,11 +609,10 @@ __device__ __forceinline__ void compute_role_full(char *ring, int vt, int lane, 
 // the buffer again. Rows past a short last chunk are dropped by the buffer range. It
 // passes the same nchunks + 2 barriers as the other waves. Lane l stores bytes
 // 16 (l % 8) .. + 15 of rows l / 8 and l / 8 + 8.
-template <int DEPTH, int NW, class Sync>
-__device__ __forceinline__ void store_wave(char *ring, int64_t nchunks, int64_t tok_rows, char *o0,
+template <int NW, class Sync>
+__device__ __forceinline__ void store_wave(const char *stage0, int64_t nchunks, int64_t tok_rows, char *o0,
                                            size_t chunk_rows, int lane, unsigned int vrow, Sync &sync) {
     static_assert(NW == 4, "a staged row is 128 bytes");
-    const char *stage0 = ring + DEPTH * slot_bytes<NW>();
     const int r = lane >> 3, p = lane & 7;
     const unsigned int off = (unsigned int)r * vrow + 16u * p;
     sync.barrier(0);  // B_0

@@ -50,7 +50,7 @@ constexpr int inter_compute_waves() { return FULL ? NW : compute_waves<NW>(); }
 template <int NW, bool FULL, bool SAVE, bool OUT>
 constexpr int inter_waves() {
     return inter_compute_waves<NW, FULL>() + kProducers +
-           ((staged_out<NW, FULL>() || staged_save<NW, SAVE, OUT>()) ? 1 : 0);
+           ((staged_out<NW, OUT>() || staged_save<NW, SAVE, OUT>()) ? 1 : 0);
 }
 template <int NW, bool FULL>
 constexpr int inter_xchg_bytes() { return FULL ? 0 : xchg_bytes<NW>(); }
@@ -95,12 +95,13 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL, SAVE, OUT>())) void kda
             return;
         }
     }
-    if constexpr (staged_out<NW, FULL>()) {
+    if constexpr (staged_out<NW, OUT>()) {
         if (wid == inter_waves<NW, FULL, SAVE, OUT>() - 1) {
             // ---- output store wave ----
             HwSync ssync;
-            store_wave<DEPTH, NW>(ring, nchunks, sc.tok_end - sc.tok_begin, reinterpret_cast<char *>(out) + tok_bytes,
-                                  chunk_rows, lane, lo.vrow, ssync);
+            store_wave<NW>(ring + DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>(), nchunks,
+                           sc.tok_end - sc.tok_begin, reinterpret_cast<char *>(out) + tok_bytes, chunk_rows, lane,
+                           lo.vrow, ssync);
             return;
         }
     }
@@ -139,22 +140,21 @@ __global__ __launch_bounds__((64 * inter_waves<NW, FULL, SAVE, OUT>())) void kda
             if (j >= 1 && j + DEPTH - 2 < nchunks) issue(j + DEPTH - 2);
         }
         barrier();  // B_nchunks
-        if (staged_out<NW, FULL>()) barrier();  // B_{nchunks+1}, for the output store wave
+        if (staged_out<NW, OUT>()) barrier();  // B_{nchunks+1}, for the output store wave
         return;
     }
 
     HwSync sync;
     if (FULL) {
-        compute_role_full<DEPTH, OUT, NW, staged_out<NW, FULL>()>(ring, wid, lane, pair, col0, sc, tok_bytes,
+        compute_role_full<DEPTH, OUT, NW, staged_out<NW, OUT>()>(ring, wid, lane, pair, col0, sc, tok_bytes,
                                                                   chunk_rows, lo, s0, out, OUT ? sT : nullptr, sync);
         return;
     }
     // chunk start states, chunk-major like the records: chunk j of this pair is H states on
     char *st = SAVE ? states + ((size_t)sc.chunk_begin * H + h) * kStateBytesBf16 : nullptr;
     const size_t sstride = (size_t)H * kStateBytesBf16;
-    compute_role<DEPTH, SAVE, OUT, NW, staged_save<NW, SAVE, OUT>()>(ring, wid, lane, pair, col0, sc, tok_bytes,
-                                                                       chunk_rows, lo, s0, out, OUT ? sT : nullptr,
-                                                                       sync, st, sstride);
+    compute_role<DEPTH, SAVE, OUT, NW, staged_save<NW, SAVE, OUT>(), staged_out<NW, OUT>()>(
+        ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, OUT ? sT : nullptr, sync, st, sstride);
 }
 
 template <int DEPTH, bool SAVE, bool OUT, int NW, bool FULL>
@@ -164,7 +164,7 @@ hipError_t launch(const void *v, const int32_t *cu_seqlens, const float *s0, voi
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const char *base = static_cast<const char *>(ws);
     const int32_t *chunk_off = reinterpret_cast<const int32_t *>(base + geo.off_chunk_off);
-    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>() + stage_bytes<NW, FULL>() +
+    constexpr size_t lds = (size_t)DEPTH * slot_bytes<NW>() + inter_xchg_bytes<NW, FULL>() + stage_bytes<NW, OUT>() +
                            save_stage_bytes<NW, SAVE, OUT>();
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     auto kern = kda_inter_bf16_kernel<DEPTH, SAVE, OUT, NW, FULL>;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void kda_fused_bf16_kernel(
         return;
     }
     HwSync sync;
-    compute_role<kFusedDepth, false, true, kNW, false>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT,
+    compute_role<kFusedDepth, false, true, kNW, false, false>(ring, wid, lane, pair, col0, sc, tok_bytes, chunk_rows, lo, s0, out, sT,
                                                 sync);
 }
 
