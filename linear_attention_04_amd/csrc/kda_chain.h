@@ -41,7 +41,7 @@ constexpr int kTiles = VD / 16;  // 16-column value tiles per head
 // load of a producer has one role and each producer issues a fixed number per chunk.
 // Only producers wait on the vector-memory counter, and they never store, so the
 // count they wait on covers their own loads alone; compute waves only read LDS,
-// compute and store.
+// compute and store (or stage their stores in LDS for a store wave, below).
 constexpr int kNW = 2;  // the default tile count (and the single-kernel ablation's)
 constexpr int kPerWave0 = 8;
 template <int NW>

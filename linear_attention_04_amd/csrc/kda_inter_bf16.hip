@@ -34,6 +34,9 @@
 // A producer waits (s_waitcnt vmcnt) for its own part of a chunk, then one
 // s_barrier per chunk publishes the slot to the compute waves (and, in the two-wave
 // form, the previous chunk's partial products between the two halves of a tile).
+// The same barrier hands a store wave what the compute waves staged in LDS: the
+// output tiles of the 4-tile forms and the saved chunk states of the 2-tile training
+// forward, which the chain's own stores would otherwise slow down (kda_chain.h).
 #include "kda_chain.h"
 #include "kda_intra_wave.h"
 
