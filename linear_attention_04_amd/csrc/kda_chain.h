@@ -272,13 +272,15 @@ __device__ __forceinline__ void chunk_part_b(const HalfOps &o, f32x4 (&S)[4], co
     for (int mm = 0; mm < 4; ++mm) S[mm] = mfma_16x16x32(o.kd[mm], db, S[mm]);  // K^d^T (Delta_hi + Delta_lo)
     if (KH == 0 && OUT) {
         const f32x4 yt = y + py;
-        // yt[i] = O[token c][column 4grp + i]: one 8-byte store per lane; rows past the
-        // end of a short chunk fall outside the descriptor and are dropped
+        // yt[i] = O[token c][column 4grp + i]: one 8-byte store (or staging write) per
+        // lane; rows past the end of a short chunk fall outside the descriptor and are dropped
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 packed = {pack_bf16x2(yt[0], yt[1]), pack_bf16x2(yt[2], yt[3])};
         if (STO) {
             *reinterpret_cast<u32x2 *>(stage + lo.stage) = packed;
-            __builtin_amdgcn_sched_barrier(0);  // as in tile_part_b
+            // kept here, a chunk step ahead of the wait on it (left to the scheduler it
+            // sinks to just before that wait)
+            __builtin_amdgcn_sched_barrier(0);
         } else {
             const __amdgpu_buffer_rsrc_t ro = rsrc(ochunk, tile_bytes<NW>(len, lo.vrow));
             __builtin_amdgcn_raw_buffer_store_b64(packed, ro, lo.out, 0, 0);
