@@ -76,6 +76,28 @@ def test_fused_fullsize_equals_split():
     assert torch.equal(out_s, out_f) and torch.equal(fs_s, fs_f)
 
 
+@pytest.mark.parametrize("name", ["fixed_h64_t8192", "fixed_h96_t8192_s0", "varlen_h96_t8192_n8"])
+def test_training_forward_fullsize_equals_prefill(name):
+    """kda_chunk_prefill_for_backward over a whole workload gives kda_chunk_prefill's
+    output and final state bit for bit. Its recurrence stages the saved chunk states
+    (2-tile form, 64 pairs) or the outputs (4-tile form, beyond 64 pairs) in LDS for a
+    store wave, here over 512 chunks per sequence."""
+    import torch
+
+    from linear_attention_04_amd import kda
+
+    w = inputs.WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    dev, _ = gu.generate_on_device(w, [])
+    out_p, fs_p = gu.run_gpu(dev)
+    out_t, fs_t, ws = kda.chunk_prefill_for_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                                     cu_seqlens=dev["cu_seqlens"],
+                                                     initial_state=dev["initial_state"])
+    torch.cuda.synchronize()
+    del ws
+    assert torch.equal(out_p, out_t) and torch.equal(fs_p, fs_t)
+
+
 def _backward_fullsize(name, keep, w=None):
     """The backward at a full workload: one kda_chunk_prefill_backward call over the
     whole batch (as the benchmark times it); the oracle's gradients for the heads in
